@@ -1,0 +1,186 @@
+"""Benchmark of one ragged paged MLA prefill step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic, device-resident
+input: plan -> gather (the batch's cache rows into a contiguous buffer) ->
+causal MLA attention.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|prefix|long|fp8|tiny]
+                  [--no-cpu-baseline] [--cpu-seconds S]
+
+value    = causal FLOPs of the step / measured step time (TFLOP/s).
+roofline = the attention kernel (the dominant one): algorithmic FLOPs per launch
+           over its average launch time from HIP events on its launch stream,
+           against the MI355X dense MFMA peak of the compute dtype.
+cpu_baseline = the float64 oracle timed on the host on a bounded sample of the
+           same workload (a subset of heads), scaled to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}      # MI355X dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mla_ragged_paged_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, kernel_hash: str):
+    """HBM bytes per attention launch from a committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"prefill_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle on the host over heads 0..k-1 of the same workload until ~budget_s of work."""
+    import numpy as np
+
+    import oracle
+    from mla_ragged_paged_amd import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, kn, v = w.q, w.k_nope, w.v
+    bro = np.concatenate([[0], np.cumsum(w.n + w.p)]).astype(np.uint32)
+    co = np.zeros(w.batch, dtype=np.uint32)
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < w.heads and time.perf_counter() - t0 < budget_s:
+        h = heads
+        oracle.mla_prefill_ragged(q[:, h:h + 1], kn[:, h:h + 1], v[:, h:h + 1], w.cache, w.spec.layer_idx,
+                                  w.page_table, w.spec.page_size, w.spec.rope_col, w.cache_lengths,
+                                  w.input_row_offsets, bro, co, w.softmax_scale, scales=w.scales)
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = workloads.causal_flops(w.n, w.p, heads)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 numpy oracle, heads 0..{heads - 1} of {w.heads} (all {w.batch} sequences), "
+                      f"{dt:.1f} s wall on the host, {threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not offered (the prefill path has no "
+              "cross-GPU step; run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from mla_ragged_paged_amd import workloads
+    from mla_ragged_paged_amd.pipeline import PrefillStep
+
+    spec = workloads.SPECS[args.workload]
+    w = workloads.build(spec)
+    flops = workloads.causal_flops(w.n, w.p, w.heads)
+    step = PrefillStep(w, "cuda:0")
+    torch.cuda.synchronize()
+    print(f"[bench] {spec.name}: B={w.batch} n={w.n.tolist()} p={w.p.tolist()} T={w.total_q} C={w.total_ctx} "
+          f"H={w.heads} causal TFLOP={flops / 1e12:.4f}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        step.plan()
+        e[1].record(stream)
+        step.gather(0)
+        e[2].record(stream)
+        step.attention(0)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    plan_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    gather_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    attn_best = min(e[2].elapsed_time(e[3]) for e in ev)
+
+    dtype = spec.dtype
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    khash = kernel_source_hash()
+    traffic = traffic_from_profiles(spec.name, khash)
+    el = 1 if dtype == "fp8" else 2
+    gather_bytes = 2.0 * w.total_ctx * w.cache.shape[4] * el
+    result = {
+        "metric": "MLA prefill TFLOP/s (causal, H=128, bf16/fp8) and % of MFMA peak, 1 GPU",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}: {spec.description}", "batch": w.batch, "heads": w.heads,
+                   "new_tokens": w.total_q, "context_tokens": w.total_ctx, "page_size": spec.page_size,
+                   "q_depth": 192, "depth": 128, "rope": 64, "seed": spec.seed},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "stages_ms": {"plan": round(plan_ms, 4), "gather": round(gather_ms, 4), "attention": round(attn_ms, 4),
+                      "attention_best": round(attn_best, 4)},
+        "pct_of_bf16_peak": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 2),
+        "gather_GBps": round(gather_bytes / (gather_ms * 1e-3) / 1e9, 1),
+        "causal_tflop_per_step": round(flops / 1e12, 5),
+        "kernel_source_hash": khash,
+    }
+    if dtype == "fp8":
+        result["pct_of_fp8_peak"] = round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 2)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

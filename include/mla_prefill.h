@@ -1,0 +1,213 @@
+/*
+ * mla_prefill.h -- C ABI of the MI355X (gfx950) ragged paged MLA prefill library.
+ *
+ * Three calls make up one prefill step of a Multi-head Latent Attention layer:
+ *
+ *   mla_prefill_plan    splits the batch's cached contexts over fixed-capacity
+ *                       buffer rows (page "generic_flare_mla_prefill_ragged_paged_plan");
+ *   mla_prefill_gather  copies one buffer row's cache entries out of the paged
+ *                       cache into a contiguous buffer (same page, description: the
+ *                       plan exists so that K/V entries can be gathered);
+ *   mla_prefill_ragged  causal attention of ragged Q [T,H,192] over the ragged
+ *                       K_nope/V buffer [rows,H,128] and the shared, paged
+ *                       K_rope [positions,1,64] (page "flare_mla_prefill";
+ *                       launch shape and argument meanings of page "mla_prefill_v2_ragged").
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host].  Device arrays are
+ *     dense and row-major in the shapes given; element types are exact.
+ *   - Every call only validates its host-side arguments and enqueues work on
+ *     `stream` (a hipStream_t passed as void*; NULL = the null stream); it never
+ *     synchronises.  The caller owns all memory and keeps it alive and unchanged
+ *     until the enqueued work has finished.  The library allocates no device
+ *     memory and keeps no state beyond its loaded code objects; calls are
+ *     thread-safe.  Outputs must not alias inputs.
+ *   - Host-checkable errors are returned before anything is enqueued (nothing
+ *     is written).  Properties of device data (monotone offsets, in-range page
+ *     ids, lengths) are preconditions that are NOT checked: violating them is
+ *     undefined behaviour.  MLA_ERR_HIP reports a failed launch
+ *     (hipGetLastError after the enqueue); mla_prefill_last_hip_error() then
+ *     returns the HIP error code.
+ *   - batch_size == 0 (or total_q_tokens == 0 for the attention) is a valid no-op.
+ */
+#ifndef MLA_PREFILL_H
+#define MLA_PREFILL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_ARG = 1,          /* a required pointer is NULL */
+  MLA_ERR_BAD_SHAPE = 2,         /* sizes are inconsistent or out of the supported range */
+  MLA_ERR_UNSUPPORTED_DTYPE = 3, /* dtype combination not offered */
+  MLA_ERR_UNSUPPORTED_DIMS = 4,  /* q_depth != 192 or depth != 128 */
+  MLA_ERR_UNSUPPORTED_MASK = 5,  /* mask kind not offered */
+  MLA_ERR_HIP = 6                /* the HIP runtime reported an error on enqueue */
+} mla_status_t;
+
+/* Element types ("flare_mla_prefill", Parameters: q is bfloat16 or float8_e4m3fn;
+ * the output is bfloat16 when q is float8_e4m3fn, else the type of q). */
+typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3FN = 1 } mla_dtype_t;
+
+/* Mask predicates ("mla_prefill_v2_ragged", Args: mask_functor). Only the causal
+ * mask is offered: key position kpos is visible to query position qpos iff
+ * kpos <= qpos. */
+typedef enum { MLA_MASK_CAUSAL = 0 } mla_mask_t;
+
+/* Largest batch the plan and gather kernels accept (their per-sequence offsets
+ * are staged in on-chip memory). */
+#define MLA_MAX_BATCH 8192
+
+/*
+ * One layer-indexed paged KV cache ("generic_flare_mla_prefill_ragged_paged_plan",
+ * Args: kv_collection and layer_idx).  The struct itself is [host]; it is read
+ * during the call only.
+ *
+ *   data          device, [num_layers][num_pages][page_size][1][row_width]
+ *                 elements of `dtype` (one KV head per cache row).
+ *   page_table    device uint32 [batch_size][max_pages_per_seq]: cache position
+ *                 pos of sequence b lives in physical page
+ *                 page_table[b][pos / page_size], slot pos % page_size.
+ *   cache_lengths device uint32 [batch_size]: tokens of sequence b cached before
+ *                 this step (its start position; "mla_prefill_v2_ragged", Args:
+ *                 k_nope).  Positions [0, cache_lengths[b] + n_b) are in the cache
+ *                 when the step runs, n_b being the step's new tokens.
+ *   rope_col      first of the 64 columns holding K_rope in a cache row
+ *                 ("flare_mla_prefill", Args: k_rope); rope_col + 64 <= row_width.
+ *   scale         device fp32 scalar, the per-tensor dequantisation scale of an
+ *                 MLA_FP8_E4M3FN cache; ignored (may be NULL) for MLA_BF16.
+ */
+typedef struct {
+  const void* data;
+  mla_dtype_t dtype;
+  uint32_t num_layers;
+  uint32_t num_pages;
+  uint32_t page_size;
+  uint32_t row_width;
+  uint32_t rope_col;
+  const uint32_t* page_table;
+  uint32_t max_pages_per_seq;
+  const uint32_t* cache_lengths;
+  const float* scale;
+} mla_paged_cache_t;
+
+/*
+ * mla_prefill_plan -- page "generic_flare_mla_prefill_ragged_paged_plan",
+ * description and Args.
+ *
+ * Sequence b has n_b = input_row_offsets[b+1] - input_row_offsets[b] new tokens
+ * and a context of L_b = kv->cache_lengths[b] + n_b cache positions.  The
+ * contexts are laid end to end in batch order (S_b = L_0 + ... + L_{b-1},
+ * C = S_B) and cut into rows of `buffer_token_size` tokens; a sequence may
+ * straddle rows.  For each row r < min(num_buffer_rows, ceil(C / cap)):
+ *   buffer_row_offsets[r][b] = clamp(S_b - r*cap, 0, cap)        (b = 0..B)
+ *   cache_offsets[r][b]      = clamp(r*cap - S_b, 0, L_b)         (b < B)
+ *   buffer_lengths[r]        = buffer_row_offsets[r][B]
+ * so row r holds sequence b's cache positions [cache_offsets[r][b], +len) at
+ * buffer slots [buffer_row_offsets[r][b], buffer_row_offsets[r][b+1]).  Rows the
+ * batch does not reach get zero offsets and buffer_lengths[r] = -1.
+ *
+ *   input_row_offsets   device uint32 [batch_size+1], non-decreasing, [0] = 0.
+ *   kv                  [host] cache descriptor; only cache_lengths is read.
+ *   layer_idx           < kv->num_layers.
+ *   buffer_token_size   cap > 0.
+ *   num_buffer_rows     R >= 1, the rows the outputs are sized for.
+ *   buffer_row_offsets  device uint32 [R][batch_size+1] (output).
+ *   cache_offsets       device uint32 [R][batch_size] (output).
+ *   buffer_lengths      device int32 [R] (output).
+ *   device_status       device int32 scalar or NULL (output): 1 when R rows
+ *                       cannot hold the batch (R*cap < C), else 0.
+ * Errors: NULL_ARG; BAD_SHAPE for cap == 0, R == 0, layer_idx out of range or
+ * batch_size > MLA_MAX_BATCH.  Exact integer arithmetic (64-bit internally).
+ */
+mla_status_t mla_prefill_plan(const uint32_t* input_row_offsets, uint32_t batch_size,
+                              const mla_paged_cache_t* kv, uint32_t layer_idx,
+                              uint32_t buffer_token_size, uint32_t num_buffer_rows,
+                              uint32_t* buffer_row_offsets, uint32_t* cache_offsets,
+                              int32_t* buffer_lengths, int32_t* device_status, void* stream);
+
+/*
+ * mla_prefill_gather -- copies one plan row's cache entries into a contiguous
+ * buffer (page "generic_flare_mla_prefill_ragged_paged_plan", description).
+ *
+ * For every b < batch_size and j < buffer_row_offsets_r[b+1] - buffer_row_offsets_r[b]:
+ *   out[buffer_row_offsets_r[b] + j][c] = cache row of sequence b at position
+ *   cache_offsets_r[b] + j, column col_begin + c, for c < col_count.
+ * Slots at or beyond buffer_row_offsets_r[batch_size] are left untouched.  A
+ * byte-exact copy in kv->dtype.
+ *
+ *   buffer_row_offsets_r  device uint32 [batch_size+1]: one row of the plan output.
+ *   cache_offsets_r       device uint32 [batch_size]: the same row's cache offsets.
+ *   col_begin, col_count  column window, col_begin + col_count <= kv->row_width, col_count >= 1.
+ *   buffer_token_size     rows of `out` (the plan's cap); buffer_row_offsets_r[B] <= it.
+ *   out                   device [buffer_token_size][col_count] elements of kv->dtype.
+ * Errors: NULL_ARG, BAD_SHAPE (column window, layer, batch_size > MLA_MAX_BATCH).
+ */
+mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx, uint32_t batch_size,
+                                const uint32_t* buffer_row_offsets_r, const uint32_t* cache_offsets_r,
+                                uint32_t col_begin, uint32_t col_count, uint32_t buffer_token_size,
+                                void* out, void* stream);
+
+/*
+ * mla_prefill_ragged -- page "flare_mla_prefill" (description, Args) with the
+ * paged k_rope operand; launch semantics of page "mla_prefill_v2_ragged".
+ *
+ * Sequence b owns query tokens t = valid_length[b] + i, i < n_b = valid_length[b+1]
+ * - valid_length[b], at cache positions qpos = kv->cache_lengths[b] + i, and keys
+ * g = cache_row_offsets[b] + j, j < cache_row_offsets[b+1] - cache_row_offsets[b],
+ * at cache positions kpos = cache_offsets[b] + j (0 + j when cache_offsets is
+ * NULL: a contiguous cache).  For every t and head h:
+ *   s_j = scale * ( sum_{d<128} q[t][h][d] * k_nope[g][h][d]
+ *                 + sum_{e<64}  q[t][h][128+e] * K_rope(b, kpos)[e] )
+ *   output[t][h][:] = sum_{j visible} softmax_j(s) * v[g][h][:]
+ * where K_rope(b, pos) is the 64-wide column window at kv->rope_col of the cache
+ * row of sequence b at position pos in layer layer_idx (one row shared by all
+ * heads), "visible" means kpos <= qpos, and a query with no visible key gets 0.
+ *
+ *   output            device [total_q_tokens][num_heads][128], output_dtype.
+ *   q                 device [total_q_tokens][num_heads][192], qkv_dtype
+ *                     (columns 0..127 pair with k_nope, 128..191 with K_rope).
+ *   k_nope, v         device [rows][num_heads][128], qkv_dtype, rows >=
+ *                     cache_row_offsets[batch_size].
+ *   k_rope            [host] paged cache descriptor; kv->dtype must be qkv_dtype.
+ *   valid_length      device uint32 [batch_size+1], ragged Q offsets,
+ *                     valid_length[batch_size] == total_q_tokens.
+ *   cache_row_offsets device uint32 [batch_size+1], ragged K/V offsets.
+ *   cache_offsets     device uint32 [batch_size] or NULL.
+ *   q_depth, depth    must be 192 and 128 (DeepSeek V2/V3 geometry).
+ *   scale             [host] softmax scale multiplying q.k.
+ *   q_scale, k_nope_scale, v_scale
+ *                     fp8 only: device fp32 per-tensor dequantisation scales
+ *                     (K_rope uses kv->scale); must be NULL for bf16.
+ *   q_max_seq_len     upper bound on n_b (bounds the launch); 0 = total_q_tokens.
+ *                     A value below some n_b is a precondition violation.
+ * Dtypes: (qkv, output) = (MLA_BF16, MLA_BF16) or (MLA_FP8_E4M3FN, MLA_BF16).
+ * Accumulation is fp32; the output is rounded to bf16 (nearest-even).
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED_DTYPE, UNSUPPORTED_DIMS,
+ * UNSUPPORTED_MASK, HIP.
+ */
+mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
+                                const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
+                                uint32_t layer_idx, const uint32_t* valid_length,
+                                const uint32_t* cache_row_offsets, const uint32_t* cache_offsets,
+                                uint32_t batch_size, uint32_t total_q_tokens, uint32_t num_heads,
+                                uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
+                                const float* q_scale, const float* k_nope_scale, const float* v_scale,
+                                uint32_t q_max_seq_len, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* mla_status_string(mla_status_t status);
+
+/* The HIP error code (hipError_t as int) behind the last MLA_ERR_HIP returned on
+ * the calling thread, 0 if none. */
+int mla_prefill_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PREFILL_H */

@@ -1,0 +1,22 @@
+"""MI355X-native ragged paged MLA prefill.
+
+The compute path is the HIP library ``libmla_prefill.so`` (built from ``csrc/``
+for gfx950).  This package is a thin binding over its C ABI: the functions below
+have the same names as the C entry points and only marshal torch tensors into
+pointers and sizes.  Importing the package fails loudly when the library has not
+been built; there is no fallback.
+"""
+from ._binding import (  # noqa: F401
+    MLA_BF16,
+    MLA_FP8_E4M3FN,
+    MLA_MASK_CAUSAL,
+    MLA_MAX_BATCH,
+    MlaError,
+    PagedCache,
+    library_path,
+    mla_prefill_gather,
+    mla_prefill_last_hip_error,
+    mla_prefill_plan,
+    mla_prefill_ragged,
+    mla_status_string,
+)

@@ -1,0 +1,179 @@
+"""ctypes binding of ``include/mla_prefill.h``: argument marshalling only.
+
+Every function takes device tensors (torch, on the current HIP device) and
+passes their data pointers, sizes and the current stream to the C entry point
+of the same name.  A non-zero status raises ``MlaError``.  Integer index arrays
+may be torch.int32 or torch.uint32 tensors (4-byte elements, values < 2**31
+when int32).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmla_prefill.so")
+
+MLA_BF16 = 0
+MLA_FP8_E4M3FN = 1
+MLA_MASK_CAUSAL = 0
+MLA_MAX_BATCH = 8192
+
+_STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_SHAPE", 3: "MLA_ERR_UNSUPPORTED_DTYPE",
+                 4: "MLA_ERR_UNSUPPORTED_DIMS", 5: "MLA_ERR_UNSUPPORTED_MASK", 6: "MLA_ERR_HIP"}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {mla_status_string(status)}"
+        if status == 6:
+            msg += f" (hipError {mla_prefill_last_hip_error()})"
+        super().__init__(msg)
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("num_layers", ctypes.c_uint32),
+                ("num_pages", ctypes.c_uint32), ("page_size", ctypes.c_uint32), ("row_width", ctypes.c_uint32),
+                ("rope_col", ctypes.c_uint32), ("page_table", ctypes.c_void_p),
+                ("max_pages_per_seq", ctypes.c_uint32), ("cache_lengths", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m mla_ragged_paged_amd.build` "
+                          "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    u32, vp, i32 = ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    cp = ctypes.POINTER(_Cache)
+    lib.mla_prefill_plan.argtypes = [vp, u32, cp, u32, u32, u32, vp, vp, vp, vp, vp]
+    lib.mla_prefill_plan.restype = i32
+    lib.mla_prefill_gather.argtypes = [cp, u32, u32, vp, vp, u32, u32, u32, vp, vp]
+    lib.mla_prefill_gather.restype = i32
+    lib.mla_prefill_ragged.argtypes = [vp, i32, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32, u32, u32, u32,
+                                       i32, ctypes.c_float, vp, vp, vp, u32, vp]
+    lib.mla_prefill_ragged.restype = i32
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_prefill_last_hip_error.argtypes = []
+    lib.mla_prefill_last_hip_error.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def mla_status_string(status: int) -> str:
+    return _lib.mla_status_string(int(status)).decode()
+
+
+def mla_prefill_last_hip_error() -> int:
+    return int(_lib.mla_prefill_last_hip_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _idx(t, name):
+    if t is None:
+        return None
+    if t.element_size() != 4 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous 4-byte integer tensor")
+    return _ptr(t)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MLA_FP8_E4M3FN
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass
+class PagedCache:
+    """Host-side description of one paged KV cache (``mla_paged_cache_t``).
+
+    data:          [num_layers, num_pages, page_size, 1, row_width] bf16 or float8_e4m3fn
+    page_table:    [batch, max_pages_per_seq] int32/uint32
+    cache_lengths: [batch] int32/uint32
+    scale:         [1] float32 device tensor (fp8 caches only)
+    """
+    data: torch.Tensor
+    page_table: torch.Tensor
+    cache_lengths: torch.Tensor
+    rope_col: int
+    scale: torch.Tensor | None = None
+
+    def as_struct(self) -> _Cache:
+        d = self.data
+        if d.dim() != 5 or d.shape[3] != 1 or not d.is_contiguous():
+            raise ValueError("cache data must be a contiguous [layers, pages, page_size, 1, row_width] tensor")
+        return _Cache(data=d.data_ptr(), dtype=_dtype_code(d), num_layers=d.shape[0], num_pages=d.shape[1],
+                      page_size=d.shape[2], row_width=d.shape[4], rope_col=self.rope_col,
+                      page_table=_idx(self.page_table, "page_table").value,
+                      max_pages_per_seq=self.page_table.shape[1],
+                      cache_lengths=_idx(self.cache_lengths, "cache_lengths").value,
+                      scale=None if self.scale is None else self.scale.data_ptr())
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MlaError(status, where)
+
+
+def mla_prefill_plan(input_row_offsets, kv: PagedCache, layer_idx, buffer_token_size, buffer_row_offsets,
+                     cache_offsets, buffer_lengths, device_status=None, stream=None):
+    """Fill the plan outputs [R][B+1], [R][B], [R] (and the status flag) for the batch."""
+    batch = input_row_offsets.shape[0] - 1
+    rows = buffer_lengths.shape[0]
+    s = kv.as_struct()
+    _check(_lib.mla_prefill_plan(_idx(input_row_offsets, "input_row_offsets"), batch, ctypes.byref(s), layer_idx,
+                                 buffer_token_size, rows, _idx(buffer_row_offsets, "buffer_row_offsets"),
+                                 _idx(cache_offsets, "cache_offsets"), _idx(buffer_lengths, "buffer_lengths"),
+                                 _idx(device_status, "device_status"), _stream(stream)), "mla_prefill_plan")
+
+
+def mla_prefill_gather(kv: PagedCache, layer_idx, buffer_row_offsets_r, cache_offsets_r, col_begin, col_count,
+                       out, stream=None):
+    """Copy one plan row's cache entries, columns [col_begin, +col_count), into out [cap, col_count]."""
+    batch = cache_offsets_r.shape[0]
+    s = kv.as_struct()
+    _check(_lib.mla_prefill_gather(ctypes.byref(s), layer_idx, batch, _idx(buffer_row_offsets_r, "bro"),
+                                   _idx(cache_offsets_r, "cache_offsets"), col_begin, col_count, out.shape[0],
+                                   _ptr(out), _stream(stream)), "mla_prefill_gather")
+
+
+def mla_prefill_ragged(output, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length, cache_row_offsets,
+                       cache_offsets, scale, q_scale=None, k_nope_scale=None, v_scale=None, q_max_seq_len=0,
+                       stream=None):
+    """Causal MLA prefill: output [T, H, 128] from q [T, H, 192] and the ragged K/V buffer."""
+    T, H, qd = q.shape
+    for t, name in ((output, "output"), (q, "q"), (k_nope, "k_nope"), (v, "v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    s = k_rope.as_struct()
+    _check(_lib.mla_prefill_ragged(_ptr(output), _dtype_code(output), _ptr(q), _dtype_code(q), _ptr(k_nope),
+                                   _ptr(v), ctypes.byref(s), layer_idx, _idx(valid_length, "valid_length"),
+                                   _idx(cache_row_offsets, "cache_row_offsets"),
+                                   _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H, qd,
+                                   k_nope.shape[2], MLA_MASK_CAUSAL, float(scale), _ptr(q_scale),
+                                   _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
+           "mla_prefill_ragged")

@@ -1,0 +1,171 @@
+// C ABI of the MLA prefill library: host-side validation, launch geometry and
+// dtype dispatch.  Declarations and the full contract live in mla_prefill.h.
+#include "mla_prefill.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+mla_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  g_last_hip_error = (int)e;
+  return MLA_ERR_HIP;
+}
+
+size_t dtype_bytes(mla_dtype_t t) { return t == MLA_FP8_E4M3FN ? 1 : 2; }
+
+bool dtype_known(mla_dtype_t t) { return t == MLA_BF16 || t == MLA_FP8_E4M3FN; }
+
+mla_status_t check_cache(const mla_paged_cache_t* kv, uint32_t layer_idx) {
+  if (!kv) return MLA_ERR_NULL_ARG;
+  if (!kv->data || !kv->page_table || !kv->cache_lengths) return MLA_ERR_NULL_ARG;
+  if (!dtype_known(kv->dtype)) return MLA_ERR_UNSUPPORTED_DTYPE;
+  if (kv->num_layers == 0 || layer_idx >= kv->num_layers || kv->num_pages == 0 || kv->page_size == 0 ||
+      kv->row_width == 0 || kv->max_pages_per_seq == 0)
+    return MLA_ERR_BAD_SHAPE;
+  return MLA_OK;
+}
+
+const uint8_t* layer_base(const mla_paged_cache_t* kv, uint32_t layer_idx) {
+  return static_cast<const uint8_t*>(kv->data) +
+         (size_t)layer_idx * kv->num_pages * kv->page_size * kv->row_width * dtype_bytes(kv->dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL_ARG: return "MLA_ERR_NULL_ARG: a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE: inconsistent or unsupported sizes";
+    case MLA_ERR_UNSUPPORTED_DTYPE: return "MLA_ERR_UNSUPPORTED_DTYPE: dtype combination not offered";
+    case MLA_ERR_UNSUPPORTED_DIMS: return "MLA_ERR_UNSUPPORTED_DIMS: q_depth must be 192 and depth 128";
+    case MLA_ERR_UNSUPPORTED_MASK: return "MLA_ERR_UNSUPPORTED_MASK: only the causal mask is offered";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown mla_status_t";
+}
+
+int mla_prefill_last_hip_error(void) { return g_last_hip_error; }
+
+mla_status_t mla_prefill_plan(const uint32_t* input_row_offsets, uint32_t batch_size, const mla_paged_cache_t* kv,
+                              uint32_t layer_idx, uint32_t buffer_token_size, uint32_t num_buffer_rows,
+                              uint32_t* buffer_row_offsets, uint32_t* cache_offsets, int32_t* buffer_lengths,
+                              int32_t* device_status, void* stream) {
+  if (!input_row_offsets || !kv || !buffer_row_offsets || !cache_offsets || !buffer_lengths) return MLA_ERR_NULL_ARG;
+  if (!kv->cache_lengths) return MLA_ERR_NULL_ARG;
+  if (kv->num_layers == 0 || layer_idx >= kv->num_layers) return MLA_ERR_BAD_SHAPE;
+  if (buffer_token_size == 0 || buffer_token_size > 0x7FFFFFFFu || num_buffer_rows == 0) return MLA_ERR_BAD_SHAPE;
+  if (batch_size > MLA_MAX_BATCH) return MLA_ERR_BAD_SHAPE;
+  mla::PlanArgs a{};
+  a.input_row_offsets = input_row_offsets;
+  a.cache_lengths = kv->cache_lengths;
+  a.batch = batch_size;
+  a.cap = buffer_token_size;
+  a.rows = num_buffer_rows;
+  a.buffer_row_offsets = buffer_row_offsets;
+  a.cache_offsets = cache_offsets;
+  a.buffer_lengths = buffer_lengths;
+  a.status = device_status;
+  return hip_status(mla::launch_plan(a, static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx, uint32_t batch_size,
+                                const uint32_t* buffer_row_offsets_r, const uint32_t* cache_offsets_r,
+                                uint32_t col_begin, uint32_t col_count, uint32_t buffer_token_size, void* out,
+                                void* stream) {
+  mla_status_t st = check_cache(kv, layer_idx);
+  if (st != MLA_OK) return st;
+  if (!buffer_row_offsets_r || !cache_offsets_r || !out) return MLA_ERR_NULL_ARG;
+  if (batch_size == 0) return MLA_OK;
+  if (batch_size > MLA_MAX_BATCH || col_count == 0 || (uint64_t)col_begin + col_count > kv->row_width ||
+      buffer_token_size == 0)
+    return MLA_ERR_BAD_SHAPE;
+  const size_t el = dtype_bytes(kv->dtype);
+  mla::GatherArgs a{};
+  a.cache = layer_base(kv, layer_idx);
+  a.page_table = kv->page_table;
+  a.buffer_row_offsets = buffer_row_offsets_r;
+  a.cache_offsets = cache_offsets_r;
+  a.out = static_cast<uint8_t*>(out);
+  a.row_bytes = (uint64_t)kv->row_width * el;
+  a.col_bytes = (uint64_t)col_begin * el;
+  a.copy_bytes = (uint64_t)col_count * el;
+  a.max_pages = kv->max_pages_per_seq;
+  a.page_size = kv->page_size;
+  a.batch = batch_size;
+  a.cap = buffer_token_size;
+  // widest copy unit that every address and size is a multiple of
+  int unit = 16;
+  while (unit > 1 && ((a.row_bytes % unit) || (a.col_bytes % unit) || (a.copy_bytes % unit) ||
+                      (reinterpret_cast<uintptr_t>(a.cache) % unit) || (reinterpret_cast<uintptr_t>(out) % unit)))
+    unit >>= 1;
+  return hip_status(mla::launch_gather(a, unit, static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
+                                const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
+                                uint32_t layer_idx, const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
+                                const float* q_scale, const float* k_nope_scale, const float* v_scale,
+                                uint32_t q_max_seq_len, void* stream) {
+  if (!output || !q || !k_nope || !v || !valid_length || !cache_row_offsets) return MLA_ERR_NULL_ARG;
+  mla_status_t st = check_cache(k_rope, layer_idx);
+  if (st != MLA_OK) return st;
+  if (q_depth != 192 || depth != 128) return MLA_ERR_UNSUPPORTED_DIMS;
+  if (mask != MLA_MASK_CAUSAL) return MLA_ERR_UNSUPPORTED_MASK;
+  if (!dtype_known(qkv_dtype) || output_dtype != MLA_BF16 || k_rope->dtype != qkv_dtype)
+    return MLA_ERR_UNSUPPORTED_DTYPE;
+  const bool fp8 = qkv_dtype == MLA_FP8_E4M3FN;
+  if (fp8 && (!q_scale || !k_nope_scale || !v_scale || !k_rope->scale)) return MLA_ERR_NULL_ARG;
+  if (!fp8 && (q_scale || k_nope_scale || v_scale)) return MLA_ERR_UNSUPPORTED_DTYPE;
+  if (batch_size == 0 || total_q_tokens == 0) return MLA_OK;
+  if (num_heads == 0) return MLA_ERR_BAD_SHAPE;
+  // 16-byte row segments: the rope window and rows must start on 16-byte boundaries
+  const uint32_t el = (uint32_t)dtype_bytes(qkv_dtype);
+  if ((k_rope->rope_col * el) % 16 || (k_rope->row_width * el) % 16 || (uint64_t)k_rope->rope_col + 64 > k_rope->row_width)
+    return MLA_ERR_BAD_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_nope) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(k_rope->data) | reinterpret_cast<uintptr_t>(output)) % 16)
+    return MLA_ERR_BAD_SHAPE;
+  const uint32_t q_max = q_max_seq_len ? q_max_seq_len : total_q_tokens;
+  const uint64_t units = (uint64_t)num_heads * batch_size * ((q_max + 127) / 128);
+  if (units > 0x7FFFFFF0ull) return MLA_ERR_BAD_SHAPE;
+
+  mla::PrefillArgs a{};
+  a.out = output;
+  a.q = q;
+  a.k_nope = k_nope;
+  a.v = v;
+  a.cache = layer_base(k_rope, layer_idx);
+  a.page_table = k_rope->page_table;
+  a.cache_lengths = k_rope->cache_lengths;
+  a.valid_length = valid_length;
+  a.cache_row_offsets = cache_row_offsets;
+  a.cache_offsets = cache_offsets;
+  a.q_scale = q_scale;
+  a.k_nope_scale = k_nope_scale;
+  a.v_scale = v_scale;
+  a.k_rope_scale = k_rope->scale;
+  a.max_pages = k_rope->max_pages_per_seq;
+  a.page_size = k_rope->page_size;
+  a.page_shift = (k_rope->page_size & (k_rope->page_size - 1)) == 0 ? (uint32_t)__builtin_ctz(k_rope->page_size)
+                                                                      : 0xFFFFFFFFu;
+  a.row_width = k_rope->row_width;
+  a.rope_col = k_rope->rope_col;
+  a.batch = batch_size;
+  a.heads = num_heads;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp8) return MLA_ERR_UNSUPPORTED_DTYPE;  // fp8 kernel not built yet
+  return hip_status(mla::launch_prefill_bf16(a, q_max, s));
+}
+
+}  // extern "C"

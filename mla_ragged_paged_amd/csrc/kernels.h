@@ -1,0 +1,70 @@
+// Kernel argument blocks and launchers of the MLA prefill library (host + device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct PlanArgs {
+  const uint32_t* input_row_offsets;  // [B+1]
+  const uint32_t* cache_lengths;      // [B]
+  uint32_t batch;
+  uint32_t cap;
+  uint32_t rows;
+  uint32_t rows_per_block;
+  uint32_t* buffer_row_offsets;       // [rows][B+1]
+  uint32_t* cache_offsets;            // [rows][B]
+  int32_t* buffer_lengths;            // [rows]
+  int32_t* status;                    // nullable
+};
+
+struct GatherArgs {
+  const uint8_t* cache;               // layer base, [pages][page_size][1][row_width] elements
+  const uint32_t* page_table;         // [B][max_pages]
+  const uint32_t* buffer_row_offsets; // [B+1]
+  const uint32_t* cache_offsets;      // [B]
+  uint8_t* out;                       // [cap][copy_bytes]
+  uint64_t row_bytes;                 // bytes of one cache row
+  uint64_t col_bytes;                 // byte offset of the copied window in a row
+  uint64_t copy_bytes;                // bytes copied per row
+  uint32_t max_pages;
+  uint32_t page_size;
+  uint32_t batch;
+  uint32_t cap;
+};
+
+struct PrefillArgs {
+  void* out;                          // bf16 [T][H][128]
+  const void* q;                      // [T][H][192]
+  const void* k_nope;                 // [rows][H][128]
+  const void* v;                      // [rows][H][128]
+  const void* cache;                  // layer base, [pages][page_size][1][row_width]
+  const uint32_t* page_table;         // [B][max_pages]
+  const uint32_t* cache_lengths;      // [B]
+  const uint32_t* valid_length;       // [B+1]
+  const uint32_t* cache_row_offsets;  // [B+1]
+  const uint32_t* cache_offsets;      // [B] or nullptr
+  const float* q_scale;               // fp8 only
+  const float* k_nope_scale;
+  const float* v_scale;
+  const float* k_rope_scale;
+  uint32_t max_pages;
+  uint32_t page_size;
+  uint32_t page_shift;                // log2(page_size) when a power of two, else 0xFFFFFFFF
+  uint32_t row_width;                 // elements per cache row
+  uint32_t rope_col;
+  uint32_t batch;
+  uint32_t heads;
+  uint32_t qtiles;                    // query tiles per sequence (launch bound)
+  uint32_t units;                     // heads * batch * qtiles
+  uint32_t units_per_xcd;             // grid size / 8
+  float scale;                        // softmax scale
+};
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, int unit, hipStream_t stream);
+hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream);
+hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream);
+
+}  // namespace mla

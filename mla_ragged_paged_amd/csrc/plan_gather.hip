@@ -1,0 +1,128 @@
+// Plan and gather kernels: page "generic_flare_mla_prefill_ragged_paged_plan"
+// (Modular MAX API docs), description and Args.
+//
+// plan:   the batch's contexts (cached prefix + new tokens of every sequence, in
+//         batch order) are cut into rows of `cap` tokens; each row records where
+//         each sequence's slice starts in the row and in the sequence's cache.
+// gather: copies one row's slices out of the paged cache into a contiguous buffer.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mla {
+
+// Every block rebuilds the batch's context prefix sums S[0..B] in LDS (B is at
+// most MLA_MAX_BATCH) and then writes the plan rows assigned to it.
+__global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
+  extern __shared__ uint64_t S[];             // [B + 1] context prefix sums
+  __shared__ uint64_t part[256];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t B = a.batch;
+  const uint32_t per = (B + 255u) / 256u;
+  const uint32_t b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  uint64_t sum = 0;
+  for (uint32_t b = b0; b < b1; ++b) {
+    const uint64_t L = (uint64_t)a.cache_lengths[b] + (uint64_t)(a.input_row_offsets[b + 1] - a.input_row_offsets[b]);
+    S[b + 1] = L;
+    sum += L;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t acc = 0;
+    for (int i = 0; i < 256; ++i) { const uint64_t t = part[i]; part[i] = acc; acc += t; }
+    S[0] = 0;
+  }
+  __syncthreads();
+  uint64_t acc = part[tid];
+  for (uint32_t b = b0; b < b1; ++b) { acc += S[b + 1]; S[b + 1] = acc; }
+  __syncthreads();
+
+  const int64_t total = (int64_t)S[B];
+  const int64_t cap = a.cap;
+  const int64_t rows_needed = (total + cap - 1) / cap;
+  if (blockIdx.x == 0 && tid == 0 && a.status) *a.status = rows_needed > (int64_t)a.rows ? 1 : 0;
+
+  const uint32_t r_begin = blockIdx.x * a.rows_per_block;
+  const uint32_t r_end = min(a.rows, r_begin + a.rows_per_block);
+  for (uint32_t r = r_begin; r < r_end; ++r) {
+    const int64_t lo = (int64_t)r * cap;
+    const bool used = (int64_t)r < rows_needed;
+    uint32_t* bro = a.buffer_row_offsets + (size_t)r * (B + 1);
+    uint32_t* co = a.cache_offsets + (size_t)r * B;
+    for (uint32_t b = tid; b <= B; b += 256) {
+      const int64_t x = (int64_t)S[b] - lo;
+      bro[b] = used ? (uint32_t)(x < 0 ? 0 : (x > cap ? cap : x)) : 0u;
+    }
+    for (uint32_t b = tid; b < B; b += 256) {
+      const int64_t L = (int64_t)(S[b + 1] - S[b]);
+      const int64_t x = lo - (int64_t)S[b];
+      co[b] = used ? (uint32_t)(x < 0 ? 0 : (x > L ? L : x)) : 0u;
+    }
+    if (tid == 0) {
+      const int64_t x = total - lo;
+      a.buffer_lengths[r] = used ? (int32_t)(x > cap ? cap : x) : -1;
+    }
+  }
+}
+
+// One thread per copy unit (UNIT bytes) of a buffer slot; consecutive threads
+// walk along a row so both the page read and the buffer write are coalesced.
+template <int UNIT>
+__global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
+  extern __shared__ uint32_t bro[];           // [B + 1] slice starts of this row
+  const uint32_t B = a.batch;
+  for (uint32_t b = threadIdx.x; b <= B; b += 256) bro[b] = a.buffer_row_offsets[b];
+  __syncthreads();
+  const uint64_t units_per_row = a.copy_bytes / UNIT;
+  const uint64_t total_units = (uint64_t)bro[B] * units_per_row;
+  for (uint64_t u = (uint64_t)blockIdx.x * 256 + threadIdx.x; u < total_units; u += (uint64_t)gridDim.x * 256) {
+    const uint32_t slot = (uint32_t)(u / units_per_row);
+    const uint32_t c = (uint32_t)(u - (uint64_t)slot * units_per_row);
+    if (slot < bro[0]) continue;              // not part of any sequence's slice
+    // sequence owning the slot: last b with bro[b] <= slot (empty slices skipped)
+    uint32_t lo = 0, hi = B;                  // invariant: bro[lo] <= slot < bro[hi]
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (bro[mid] <= slot) lo = mid; else hi = mid;
+    }
+    const uint32_t b = lo;
+    const uint32_t pos = a.cache_offsets[b] + (slot - bro[b]);
+    const uint32_t page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
+    const size_t row = (size_t)page * a.page_size + pos % a.page_size;
+    const uint8_t* src = a.cache + row * a.row_bytes + a.col_bytes + (size_t)c * UNIT;
+    uint8_t* dst = a.out + (size_t)slot * a.copy_bytes + (size_t)c * UNIT;
+    if constexpr (UNIT == 16) st16(dst, ld16(src));
+    else if constexpr (UNIT == 8) *reinterpret_cast<uint64_t*>(dst) = *reinterpret_cast<const uint64_t*>(src);
+    else if constexpr (UNIT == 4) *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+    else if constexpr (UNIT == 2) *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+    else *dst = *src;
+  }
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
+  const uint32_t rows_per_block = 16;
+  const uint32_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  PlanArgs args = a;
+  args.rows_per_block = rows_per_block;
+  const size_t lds = sizeof(uint64_t) * (a.batch + 1);
+  hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(256), lds, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, int unit, hipStream_t stream) {
+  const uint64_t units = (uint64_t)a.cap * (a.copy_bytes / unit);
+  uint64_t blocks = (units + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks == 0) blocks = 1;
+  const size_t lds = sizeof(uint32_t) * (a.batch + 1);
+  switch (unit) {
+    case 16: hipLaunchKernelGGL(gather_kernel<16>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+    case 8: hipLaunchKernelGGL(gather_kernel<8>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+    case 4: hipLaunchKernelGGL(gather_kernel<4>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+    case 2: hipLaunchKernelGGL(gather_kernel<2>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+    default: hipLaunchKernelGGL(gather_kernel<1>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

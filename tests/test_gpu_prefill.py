@@ -1,0 +1,129 @@
+"""Attention on the GPU against the float64 oracle.
+
+Bar (bf16 inputs and output): max |gpu - oracle| <= 1e-2 on N(0, 1) inputs.
+Small problems are compared on every output; the full-size workloads on a
+sample of (token, head) outputs that the oracle evaluates one by one, plus
+properties that hold at any size (finite, deterministic).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_ragged_paged_amd import workloads
+from mla_ragged_paged_amd.pipeline import PrefillStep
+from tests.gpu_util import check_plan, get_workload, oracle_full, oracle_rows, report, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+BAR_BF16 = 1e-2
+
+
+def _run(w, cap=None):
+    step = PrefillStep(w, "cuda", cap=cap)
+    step.run()
+    torch.cuda.synchronize()
+    return step
+
+
+def test_tiny_workload_every_output():
+    w = get_workload("tiny")
+    step = _run(w)
+    bro, co, _ = check_plan(step, w)
+    ref = oracle_full(w, bro[0], co[0])
+    assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, "tiny") <= BAR_BF16
+
+
+SMALL = [
+    dict(n=[130, 1, 257, 0, 64], p=[0, 300, 77, 5, 0], heads=4, ps=16, width=576, rope=512),
+    dict(n=[200], p=[1000], heads=3, ps=128, width=576, rope=512),
+    dict(n=[150, 70], p=[33, 0], heads=2, ps=48, width=576, rope=512),      # page size not a power of two
+    dict(n=[40, 7], p=[10, 3], heads=2, ps=1, width=64, rope=0),            # one token per page, rope-only rows
+    dict(n=[1, 1, 2], p=[0, 9, 0], heads=5, ps=16, width=128, rope=64),     # single-token sequences
+    dict(n=[513], p=[0], heads=2, ps=128, width=576, rope=512),             # 4 full tiles + 1 row
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_ragged_every_output(case):
+    kw = SMALL[case]
+    say(f"small ragged case {kw}")
+    spec = workloads.Spec("small", len(kw["n"]), (0, 0), (0, 0), kw["heads"], kw["ps"], True, "bf16",
+                          row_width=kw["width"], rope_col=kw["rope"], seed=70 + case)
+    w = workloads.build(spec, n=kw["n"], p=kw["p"])
+    step = _run(w)
+    bro, co, _ = check_plan(step, w)
+    ref = oracle_full(w, bro[0], co[0])
+    assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, f"small{case}") <= BAR_BF16
+
+
+def _row_buffers(w, bro_r, co_r):
+    """K_nope / V of one plan row, laid out as a gather of K/V entries would leave them."""
+    L = w.n + w.p
+    start = np.concatenate([[0], np.cumsum(L)])
+    cap = int(bro_r[-1]) if bro_r[-1] > 0 else 1
+    idx = np.zeros(cap, dtype=np.int64)
+    for b in range(w.batch):
+        for j in range(int(bro_r[b + 1]) - int(bro_r[b])):
+            idx[int(bro_r[b]) + j] = start[b] + int(co_r[b]) + j
+    it = torch.from_numpy(idx)
+    return w.k_nope.index_select(0, it).contiguous(), w.v.index_select(0, it).contiguous()
+
+
+def test_several_buffer_rows():
+    """Capacity below the batch's context: every row is attended separately (keys of that row only)."""
+    spec = workloads.Spec("rows", 3, (0, 0), (0, 0), 2, 16, True, "bf16", row_width=576, rope_col=512, seed=80)
+    w = workloads.build(spec, n=[90, 20, 150], p=[60, 0, 200])
+    step = PrefillStep(w, "cuda", cap=160)
+    step.plan()
+    torch.cuda.synchronize()
+    bro, co, bl = check_plan(step, w)
+    assert step.rows >= 3
+    for r in range(step.rows):
+        kn, v = _row_buffers(w, bro[r], co[r])
+        out = torch.zeros_like(step.out)
+        step.attention(r, k_nope=kn.cuda(), v=v.cuda(), out=out)
+        torch.cuda.synchronize()
+        ref = oracle_full(w, bro[r], co[r], k_nope=kn, v=v)
+        assert report(out.float().cpu().numpy(), ref, BAR_BF16, f"row{r}") <= BAR_BF16
+
+
+def test_contiguous_cache_without_offsets_matches_zero_offsets():
+    w = get_workload("tiny")
+    step = _run(w)
+    first = step.out.clone()
+    step.out.zero_()
+    step.attention(0, cache_offsets=None)
+    torch.cuda.synchronize()
+    assert torch.equal(first, step.out)
+
+
+@pytest.mark.parametrize("name", ["dsv3", "prefix", "long"])
+def test_full_size_workloads_sampled(name):
+    w = get_workload(name)
+    say(f"{name}: B={w.batch} T={w.total_q} C={w.total_ctx} H={w.heads}")
+    step = _run(w)
+    bro, co, _ = check_plan(step, w)
+    out = step.out.float()
+    assert bool(torch.isfinite(out).all())
+    rows = sample_rows(w, 160, seed=7)
+    ref = oracle_rows(w, rows, bro[0], co[0])
+    got = np.stack([out[t, h].cpu().numpy() for t, h in rows])
+    assert report(got, ref, BAR_BF16, name) <= BAR_BF16
+
+
+def test_bit_identical_reruns_and_launch_bound():
+    w = get_workload("dsv3")
+    step = _run(w)
+    first = step.out.clone()
+    step.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first, step.out)
+    # a looser launch bound on the query length only adds empty work units
+    step.out.zero_()
+    import mla_ragged_paged_amd as m
+    m.mla_prefill_ragged(step.out, step.q, step.k_nope, step.v, step.kv, 0, step.input_row_offsets,
+                         step.buffer_row_offsets[0], step.cache_offsets[0], w.softmax_scale,
+                         q_max_seq_len=w.total_q)
+    torch.cuda.synchronize()
+    assert torch.equal(first, step.out)

@@ -1,0 +1,87 @@
+"""The C-ABI library loads and exports every entry point its header declares (CPU only).
+
+Only host-side validation paths are called here: each returns its error code
+before any HIP call, so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_prefill.h")
+LIB = os.path.join(ROOT, "mla_ragged_paged_amd", "libmla_prefill.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built: run python -m mla_ragged_paged_amd.build")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_plan",
+                                    "mla_prefill_ragged", "mla_status_string"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    lib.mla_status_string.restype = ctypes.c_char_p
+    for code in range(7):
+        assert lib.mla_status_string(code).decode().startswith("MLA_")
+    assert lib.mla_status_string(99) == b"unknown mla_status_t"
+
+
+def test_binding_validation_without_gpu():
+    import mla_ragged_paged_amd as m
+    # NULL pointers are rejected before anything is enqueued
+    lib = m._binding._lib
+    assert lib.mla_prefill_plan(None, 1, None, 0, 8, 1, None, None, None, None, None) == 1
+    assert lib.mla_prefill_gather(None, 0, 1, None, None, 0, 1, 1, None, None) == 1
+    assert m.mla_prefill_last_hip_error() == 0
+    assert "NULL" in m.mla_status_string(1)
+
+
+def test_validation_codes_without_gpu():
+    import mla_ragged_paged_amd._binding as b
+    lib = b._lib
+    dummy = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    s = b._Cache(data=16, dtype=0, num_layers=1, num_pages=1, page_size=16, row_width=64, rope_col=0,
+                 page_table=16, max_pages_per_seq=1, cache_lengths=16, scale=None)
+    ref = ctypes.byref(s)
+    # plan: zero capacity, zero rows, batch too large, layer out of range
+    assert lib.mla_prefill_plan(dummy, 1, ref, 0, 0, 1, dummy, dummy, dummy, None, None) == 2
+    assert lib.mla_prefill_plan(dummy, 1, ref, 0, 8, 0, dummy, dummy, dummy, None, None) == 2
+    assert lib.mla_prefill_plan(dummy, 8193, ref, 0, 8, 1, dummy, dummy, dummy, None, None) == 2
+    assert lib.mla_prefill_plan(dummy, 1, ref, 1, 8, 1, dummy, dummy, dummy, None, None) == 2
+    # gather: column window beyond the row
+    assert lib.mla_prefill_gather(ref, 0, 1, dummy, dummy, 60, 8, 4, dummy, None) == 2
+    # attention: dims, mask, dtype combinations, fp8 without scales, bf16 with scales, bad rope window
+    args = lambda **kw: [kw.get("out", dummy), kw.get("odt", 0), dummy, kw.get("qdt", 0), dummy, dummy, ref, 0,
+                         dummy, dummy, None, 1, 4, 2, kw.get("qd", 192), kw.get("d", 128), kw.get("mask", 0),
+                         ctypes.c_float(0.07), kw.get("qs"), None, None, 0, None]
+    assert lib.mla_prefill_ragged(*args(qd=576)) == 4
+    assert lib.mla_prefill_ragged(*args(d=512)) == 4
+    assert lib.mla_prefill_ragged(*args(mask=1)) == 5
+    assert lib.mla_prefill_ragged(*args(odt=1)) == 3
+    assert lib.mla_prefill_ragged(*args(qdt=1)) == 3        # cache dtype bf16 != q dtype
+    assert lib.mla_prefill_ragged(*args(qs=dummy)) == 3     # scales given for bf16
+    assert lib.mla_prefill_ragged(*args(out=None)) == 1
+    s.rope_col = 8
+    assert lib.mla_prefill_ragged(*args()) == 2             # rope window past the row
+    s.rope_col = 0
+    s.dtype = 1
+    fp8 = args(qdt=1)
+    assert lib.mla_prefill_ragged(*fp8) == 1                # fp8 needs every scale
