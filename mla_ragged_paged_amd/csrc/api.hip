@@ -135,6 +135,10 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_nope) | reinterpret_cast<uintptr_t>(v) |
        reinterpret_cast<uintptr_t>(k_rope->data) | reinterpret_cast<uintptr_t>(output)) % 16)
     return MLA_ERR_BAD_SHAPE;
+  // the kernels address one sequence's rows and one cache layer with 32-bit byte offsets
+  const uint64_t layer_bytes = (uint64_t)k_rope->num_pages * k_rope->page_size * k_rope->row_width * el;
+  if (layer_bytes >= (1ull << 32) || (uint64_t)total_q_tokens * num_heads * q_depth * el >= (1ull << 32))
+    return MLA_ERR_BAD_SHAPE;
   const uint32_t q_max = q_max_seq_len ? q_max_seq_len : total_q_tokens;
   const uint64_t units = (uint64_t)num_heads * batch_size * ((q_max + 127) / 128);
   if (units > 0x7FFFFFF0ull) return MLA_ERR_BAD_SHAPE;
@@ -163,6 +167,11 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
   a.batch = batch_size;
   a.heads = num_heads;
   a.scale = scale;
+  a.cache_bytes = (uint32_t)layer_bytes;
+  {
+    const float c = (scale < 0.f ? -scale : scale) * 1.4426950408889634f;
+    a.scale_log2 = c > 1e-30f ? c : 1e-30f;  // scale 0: every visible key weighs the same
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp8) return MLA_ERR_UNSUPPORTED_DTYPE;  // fp8 kernel not built yet
   return hip_status(mla::launch_prefill_bf16(a, q_max, s));

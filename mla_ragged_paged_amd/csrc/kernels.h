@@ -54,12 +54,14 @@ struct PrefillArgs {
   uint32_t page_shift;                // log2(page_size) when a power of two, else 0xFFFFFFFF
   uint32_t row_width;                 // elements per cache row
   uint32_t rope_col;
+  uint32_t cache_bytes;               // bytes of one layer of the cache (< 4 GiB)
   uint32_t batch;
   uint32_t heads;
   uint32_t qtiles;                    // query tiles per sequence (launch bound)
   uint32_t units;                     // heads * batch * qtiles
   uint32_t units_per_xcd;             // grid size / 8
-  float scale;                        // softmax scale
+  float scale;                        // softmax scale (its sign is applied to Q)
+  float scale_log2;                   // max(|scale| * log2(e), 1e-30)
 };
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);

@@ -5,21 +5,35 @@
 //
 // Work unit = (head h, sequence b, query tile of BM = 128 rows).  A workgroup of
 // four waves owns one unit; wave w owns queries [32w, 32w+32) of the tile.
-// Keys stream through LDS in tiles of BN = 64: K (128 nope columns from k_nope
-// plus the 64 shared K_rope columns read through the page table) and V, both
-// row-major, with the next tile's global loads in flight while the current one
-// is consumed.
+//
+// Keys stream through LDS in tiles of BN = 64, two stages deep.  Each tile is
+// three regions -- K_nope [64][128], K_rope [64][64] (read through the page
+// table, shared by all heads) and V [64][128] -- filled by buffer loads that
+// write LDS directly (no register staging).  A 16-byte chunk c of row r is
+// stored at chunk c ^ swz(r) of its row, which keeps both the MFMA operand reads
+// and the transposed V reads free of bank conflicts without padding.  One
+// barrier per tile: it publishes tile k and retires tile k-1's stage, which the
+// loads of tile k+1 then overwrite while tile k is consumed.
 //
 // Per wave and key tile, on the 32x32x16 bf16 MFMA:
 //   S^T = K . Q^T  (A = K rows from LDS, B = the wave's Q held in registers),
 //        so each lane owns one query column and 32 of the tile's 64 keys:
 //        row max / sum need one exchange between the wave's two 32-lane halves;
-//   online softmax in the exp2 domain (scale * log2 e folded in), masking only
-//        on tiles that straddle the causal diagonal or the ragged tail;
+//   online softmax in the exp2 domain: p = exp2(s*c - m*c), c = |scale|*log2(e)
+//        (a negative scale is applied by flipping the sign of Q, which is
+//        exact).  The running max m only moves when some row's tile max
+//        exceeds it by more than RESCALE_LOG2 (in log2 units), so the O
+//        rescale is skipped on most tiles; p then stays below 2^RESCALE_LOG2.
+//        p is rounded to bf16 once and the row sum is taken over the rounded
+//        values (v_dot2 against (1, 1)), so the weights applied to V are
+//        normalised exactly.  Masks are applied only on tiles that straddle
+//        the causal diagonal or the end of the sequence's keys;
 //   O^T += V^T . P^T (A = V read transposed out of row-major LDS with
-//        ds_read_b64_tr_b16, B = P^T straight from the S^T registers after a
-//        bf16 rounding).  The 16 keys of one MFMA step are taken in the order
-//        the S^T accumulator holds them; V is read in that same order.
+//        ds_read_b64_tr_b16, B = P^T straight from the S^T registers).  The 16
+//        keys of one MFMA step are taken in the order the S^T accumulator
+//        holds them; V is read in that same order.
+// Buffer descriptors are sized to the valid rows, so loads past the ragged
+// tail return zeros without branches.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,25 +43,38 @@ namespace {
 constexpr int BM = 128;            // queries per workgroup
 constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
-constexpr int DQK = 192, DNOPE = 128, DROPE = 64, DV = 128;
-constexpr int KS = DQK + 8;        // LDS row stride of K (bf16 elements)
-constexpr int VS = DV + 32;        // LDS row stride of V (bf16 elements)
+constexpr int DQK = 192, DNOPE = 128, DV = 128;
+constexpr float RESCALE_LOG2 = 8.0f;
 
-struct Tile {                      // one thread's share of a K/V tile, in flight
-  i32x4 kn[4];
-  i32x4 kr[2];
-  i32x4 v[4];
-};
+// LDS stage layout (bytes)
+constexpr int KN_OFF = 0;                      // K_nope [64 rows][16 chunks of 16 B]
+constexpr int KR_OFF = KN_OFF + BN * 256;      // K_rope [64 rows][8 chunks]
+constexpr int V_OFF = KR_OFF + BN * 128;       // V      [64 rows][16 chunks]
+constexpr int STAGE = V_OFF + BN * 256;        // 40 KiB
+constexpr int LDS_BYTES = 2 * STAGE;
 
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ i32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// 64 lanes x 16 B from the buffer at per-lane byte offsets into 1 KiB of LDS at `dst`
+// (lane i lands at dst + 16 i).
+__device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, MLA_LDS void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+
 }  // namespace
 
 __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * VS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
   // ---- work unit: XCD-aware decode.  Workgroup ids go round-robin over the 8
   // XCDs, so id % 8 picks a contiguous range of the (head, sequence, tile)
@@ -66,195 +93,229 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   if (i0 >= n) return;
 
   const uint32_t H = a.heads;
-  const uint32_t p = a.cache_lengths[b];
+  const int32_t p = (int32_t)a.cache_lengths[b];
   const uint32_t g0 = a.cache_row_offsets[b];
-  const uint32_t len = a.cache_row_offsets[b + 1] - g0;
-  const uint32_t c0 = a.cache_offsets ? a.cache_offsets[b] : 0u;
-  const uint32_t i_last = min(n, i0 + BM) - 1u;
+  const int32_t len = (int32_t)(a.cache_row_offsets[b + 1] - g0);
+  const int32_t c0 = a.cache_offsets ? (int32_t)a.cache_offsets[b] : 0;
+  const int32_t i_last = (int32_t)min(n, i0 + BM) - 1;
   // keys some query of the tile can see: c0 + j <= p + i_last
-  const int64_t jlim = (int64_t)p + i_last - c0 + 1;
-  const uint32_t jend = jlim <= 0 ? 0u : (uint32_t)min<int64_t>(jlim, len);
-  const uint32_t nkt = (jend + BN - 1) / BN;
+  const int32_t jend = max(0, min(p + i_last - c0 + 1, len));
+  const int32_t nkt = (jend + BN - 1) / BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int li = lane & 31, hf = lane >> 5;
-  const uint32_t iw0 = i0 + 32u * w;                 // wave's first query
-  const bool wave_rows = iw0 < n;
-  const uint32_t my_i = iw0 + li;                    // this lane's query column
-  const bool row_valid = my_i < n;
-  const int64_t my_qpos = (int64_t)p + my_i;
-  const int64_t wq_first = (int64_t)p + iw0;
-  const int64_t wq_last = (int64_t)p + min(n, iw0 + 32u) - 1;
+  const int32_t iw0 = (int32_t)i0 + 32 * w;          // wave's first query
+  const bool wave_rows = iw0 < (int32_t)n;
+  const int32_t my_i = iw0 + li;                      // this lane's query column
+  const int32_t wq_first = p + iw0;
+  const int32_t wq_last = p + min((int32_t)n, iw0 + 32) - 1;
 
-  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ KN = static_cast<const uint16_t*>(a.k_nope);
-  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
-  const uint16_t* __restrict__ CR = static_cast<const uint16_t*>(a.cache);
+  // ---- buffer descriptors (byte offsets relative to this unit's first row)
+  const uint32_t q_row = H * DQK * 2, kv_row = H * DNOPE * 2;
+  const auto q_rs = rsrc(static_cast<const uint8_t*>(a.q) + ((size_t)t0 * H + h) * DQK * 2,
+                         (n - 1) * q_row + DQK * 2);
+  const uint32_t kv_bytes = jend > 0 ? (uint32_t)(jend - 1) * kv_row + DNOPE * 2 : 0u;
+  const auto kn_rs = rsrc(static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE * 2, kv_bytes);
+  const auto v_rs = rsrc(static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE * 2, kv_bytes);
+  const auto cr_rs = rsrc(a.cache, a.cache_bytes);
   const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
+  const uint32_t cache_row = a.row_width * 2;
+
+  // ---- V stages start as zeros: rows past the keys are never NaN garbage
+  for (int i = tid; i < 2 * BN * 16; i += NT) {
+    const int s = i / (BN * 16), k = i % (BN * 16);
+    *reinterpret_cast<i32x4*>(&lds[s * STAGE + V_OFF + 16 * k]) = i32x4{0, 0, 0, 0};
+  }
 
   // ---- Q^T operands: lane (li, hf) holds q[t][h][16ks + 8hf .. +7] for its query
+  // (rows past the sequence read as zeros; a negative scale flips the sign of Q)
   bf16x8 qop[12];
   {
-    const uint32_t qi = row_valid ? my_i : 0u;
-    const uint16_t* qrow = Q + ((size_t)(t0 + qi) * H + h) * DQK + hf * 8;
+    const int sign = a.scale < 0.f ? (int)0x80008000 : 0;
+    const uint32_t qoff = (uint32_t)my_i * q_row + hf * 16;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) {
-      i32x4 x = ld16(qrow + ks * 16);
-      if (!row_valid) x = i32x4{0, 0, 0, 0};
+      i32x4 x = bload16(q_rs, qoff + ks * 32);
+      x ^= sign;
       qop[ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  auto load_tile = [&](uint32_t kt, Tile& tl) {
-    const uint32_t j0 = kt * BN;
+  // ---- this lane's slots of a tile load (one 1 KiB load = 64 slots of 16 B)
+  // K_nope / V: load m = 4w + u covers rows 4m .. 4m+3, slot lane -> row 4m + lane/16,
+  // stored chunk lane%16 holds source chunk (lane%16) ^ swz(row).
+  uint32_t kn_off[4], v_off[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {                    // nope and V: 64 rows x 16 chunks
-      const int c = tid + NT * u;
-      const uint32_t j = j0 + (c >> 4);
-      const int col = (c & 15) * 8;
-      i32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-      if (j < jend) {
-        const size_t off = ((size_t)(g0 + j) * H + h) * DNOPE + col;
-        kx = ld16(KN + off);
-        vx = ld16(V + off);
-      }
-      tl.kn[u] = kx;
-      tl.v[u] = vx;
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int r = 16 * w + 4 * u + (lane >> 4);
+    const int cs = lane & 15;
+    kn_off[u] = (uint32_t)r * kv_row + 16u * (uint32_t)(cs ^ (r & 15));
+    v_off[u] = (uint32_t)r * kv_row + 16u * (uint32_t)(cs ^ (4 * (r & 3)));
+  }
+  // K_rope: load m = 2w + u covers rows 8m .. 8m+7, slot lane -> row 8m + lane/8
+  int kr_row[2], kr_chunk[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {                    // rope: 64 rows x 8 chunks
-      const int c = tid + NT * u;
-      const uint32_t j = j0 + (c >> 3);
-      const int col = (c & 7) * 8;
-      i32x4 rx = {0, 0, 0, 0};
-      if (j < jend) {
-        const uint32_t pos = c0 + j;
-        uint32_t page, slot;
-        if (a.page_shift < 32u) { page = PT[pos >> a.page_shift]; slot = pos & (a.page_size - 1u); }
-        else { page = PT[pos / a.page_size]; slot = pos % a.page_size; }
-        rx = ld16(CR + ((size_t)page * a.page_size + slot) * a.row_width + a.rope_col + col);
-      }
-      tl.kr[u] = rx;
-    }
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * w + 8 * u + (lane >> 3);
+    kr_row[u] = r;
+    kr_chunk[u] = (lane & 7) ^ ((r >> 1) & 7);
+  }
+  auto page_of = [&](int32_t kt, int u) -> uint32_t {
+    const int32_t j = min(kt * BN + kr_row[u], jend - 1);   // clamped: always a valid position
+    const uint32_t pos = (uint32_t)(c0 + j);
+    return a.page_shift < 32u ? PT[pos >> a.page_shift] : PT[pos / a.page_size];
   };
-  auto store_tile = [&](const Tile& tl) {
+  auto issue_tile = [&](int32_t kt, int stage, const uint32_t (&pg)[2]) {
+    const uint32_t jrow = (uint32_t)(kt * BN) * kv_row;
+    MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * STAGE;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = tid + NT * u;
-      const int row = c >> 4, col = (c & 15) * 8;
-      *reinterpret_cast<i32x4*>(&Ks[row * KS + col]) = tl.kn[u];
-      *reinterpret_cast<i32x4*>(&Vs[row * VS + col]) = tl.v[u];
+      const int m = 4 * w + u;
+      bload_lds(kn_rs, jrow + kn_off[u], st + KN_OFF + m * 1024);
+      bload_lds(v_rs, jrow + v_off[u], st + V_OFF + m * 1024);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int c = tid + NT * u;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<i32x4*>(&Ks[row * KS + DNOPE + col]) = tl.kr[u];
+      const int m = 2 * w + u;
+      const int32_t j = min(kt * BN + kr_row[u], jend - 1);
+      const uint32_t pos = (uint32_t)(c0 + j);
+      const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
+      const uint32_t off = (pg[u] * a.page_size + slot) * cache_row + a.rope_col * 2 + 16u * kr_chunk[u];
+      bload_lds(cr_rs, off, st + KR_OFF + m * 1024);
     }
   };
 
-  // ---- running softmax state (exp2 domain) and output accumulator O^T
-  const float c_log2 = a.scale * 1.4426950408889634f;
-  float m_run = -1e30f;                              // finite: exp2(m_old - m_new) stays defined
+  // ---- per-lane LDS read offsets (within a stage)
+  // K operand: row R = 32kb + li, chunk 2ks + hf stored at chunk ^ swz(R)
+  uint32_t kn_rd[8], kr_rd[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kn_rd[ks] = KN_OFF + li * 256 + 16 * ((2 * ks + hf) ^ (li & 15));
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) kr_rd[ks] = KR_OFF + li * 128 + 16 * ((2 * ks + hf) ^ ((li >> 1) & 7));
+  // V transposed reads (ds_read_b64_tr_b16: lane 16g+4e+c of a 16-lane group supplies
+  // row e, columns 4c..4c+3): row = 16kk + 4(g>>1) + e (+8), dv = 32d + 16(g&1) + 4c
+  const int tr_g = lane >> 4, tr_e = (lane >> 2) & 3, tr_c = lane & 3;
+  const int tr_row = 4 * (tr_g >> 1) + tr_e;
+  uint32_t v_rd[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int chunk = 4 * d + 2 * (tr_g & 1) + (tr_c >> 1);
+    v_rd[d] = V_OFF + tr_row * 256 + 16 * (chunk ^ (4 * tr_e)) + 8 * (tr_c & 1);
+  }
+
+  // ---- running softmax state (raw score units) and output accumulator O^T
+  const float c = a.scale_log2;                      // |scale| * log2(e), > 0
+  const float thr = RESCALE_LOG2 / c;                // rescale threshold in raw units
+  float m_run = -1e30f;                              // finite, so (m_old - m_new) stays defined
+  float mc = m_run * c;
   float l_run = 0.f;                                 // this lane's share of the row sum
   f32x16 o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = f32x16{};
 
-  // transposed-read source address of this lane inside a 16-key MFMA step
-  // (see ds_read_b64_tr_b16: lane 16g+4e+c supplies row e, columns 4c..4c+3)
-  const int tr_g = lane >> 4, tr_e = (lane >> 2) & 3, tr_c = lane & 3;
-  const int tr_row = 4 * (tr_g >> 1) + tr_e;         // key within the step (+8 for the second read)
-  const int tr_col = (tr_g & 1) * 16 + 4 * tr_c;     // dv within a 32-wide block
-
-  Tile tl;
+  uint32_t pg_next[2] = {0u, 0u};
   if (nkt > 0) {
-    load_tile(0, tl);
-    store_tile(tl);
+    const uint32_t pg0[2] = {page_of(0, 0), page_of(0, 1)};
+    __syncthreads();                                 // V zero-fill done before any load lands
+    issue_tile(0, 0, pg0);
+    pg_next[0] = page_of(1, 0);
+    pg_next[1] = page_of(1, 1);
   }
-  __syncthreads();
 
-  for (uint32_t kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) load_tile(kt + 1, tl);
-    const uint32_t j0 = kt * BN;
-    const int64_t kfirst = (int64_t)c0 + j0;
-    if (wave_rows && kfirst <= wq_last) {
-      const bool full = (j0 + BN <= len) && (kfirst + BN - 1 <= wq_first);
+  for (int32_t kt = 0; kt < nkt; ++kt) {
+    const int stage = kt & 1;
+    // publish tile kt (every wave's loads done) and retire stage (kt+1)&1
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      issue_tile(kt + 1, stage ^ 1, pg_next);
+      pg_next[0] = page_of(kt + 2, 0);
+      pg_next[1] = page_of(kt + 2, 1);
+    }
+    const int32_t j0 = kt * BN;
+    if (wave_rows && c0 + j0 <= wq_last) {
+      const uint8_t* st = lds + stage * STAGE;
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + li) * KS + ks * 16 + hf * 8]);
+          const uint32_t off = ks < 8 ? kn_rd[ks] + kb * 32 * 256 : kr_rd[ks - 8] + kb * 32 * 128;
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + off);
           s[kb] = mfma_bf16(ka, qop[ks], s[kb]);
         }
       }
-      // scale, mask, row max.  s[kb][r] is key j0 + 32kb + 8(r/4) + 4hf + r%4.
+      // s[kb][r] is key j0 + 32kb + 4hf + roff(r), roff(r) = 8(r/4) + r%4
+      const bool full = (j0 + BN <= len) && (c0 + j0 + BN - 1 <= wq_first);
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int32_t kbase = j0 + 32 * kb + 4 * hf;
+          const int32_t lim = min(len - 1 - kbase, p + my_i - c0 - kbase);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int32_t roff = 8 * (r >> 2) + (r & 3);
+            s[kb][r] = roff <= lim ? s[kb][r] : -INFINITY;
+          }
+        }
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * c_log2;
-          if (!full) {
-            const uint32_t j = j0 + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-            const bool vis = (j < len) && ((int64_t)c0 + j <= my_qpos);
-            x = vis ? x : -INFINITY;
-          }
-          s[kb][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = max_across_halves(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        mc = m_run * c;
+        l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
-          s[kb][r] = e;
-          psum += e;
-        }
+        for (int d = 0; d < 4; ++d) o[d] *= alpha;
       }
-      l_run = l_run * alpha + psum;
+      uint32_t pw[16];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) o[d] *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          pw[8 * kb + x] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * x], c, -mc)),
+                                       __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * x + 1], c, -mc)));
+      {
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int x = 0; x < 16; x += 2) {
+          ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x]), ones, ps0, false);
+          ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x + 1]), ones, ps1, false);
+        }
+        l_run += ps0 + ps1;
+      }
 
       // O^T += V^T P^T, four 16-key steps
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int kb = kk >> 1, sub = kk & 1;
-        uint32_t pw[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) pw[x] = pack_bf16x2(s[kb][8 * sub + 2 * x], s[kb][8 * sub + 2 * x + 1]);
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
-        const int key = kk * 16 + tr_row;
+        const i32x4 pv = {(int)pw[4 * kk], (int)pw[4 * kk + 1], (int)pw[4 * kk + 2], (int)pw[4 * kk + 3]};
+        const bf16x8 pop = __builtin_bit_cast(bf16x8, pv);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const uint16_t* base = &Vs[key * VS + d * 32 + tr_col];
+          const MLA_LDS uint8_t* base = (const MLA_LDS uint8_t*)st + v_rd[d] + kk * 16 * 256;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base + 8 * VS));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, i32x4{__builtin_bit_cast(i32x2, lo)[0], __builtin_bit_cast(i32x2, lo)[1],
-                                                             __builtin_bit_cast(i32x2, hi)[0], __builtin_bit_cast(i32x2, hi)[1]});
-          o[d] = mfma_bf16(va, pop, o[d]);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base + 8 * 256));
+          typedef __attribute__((ext_vector_type(8))) short i16x8;
+          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[d] = mfma_bf16(__builtin_bit_cast(bf16x8, both), pop, o[d]);
         }
       }
-    }
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      store_tile(tl);
-      __syncthreads();
     }
   }
 
   // ---- epilogue: combine the two halves' row sums, normalise, round to bf16
   const float l_tot = l_run + swap_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row_valid) {
+  if (my_i < (int32_t)n) {
     uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(t0 + my_i) * H + h) * DV;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {

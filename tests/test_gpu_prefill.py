@@ -127,3 +127,15 @@ def test_bit_identical_reruns_and_launch_bound():
                          q_max_seq_len=w.total_q)
     torch.cuda.synchronize()
     assert torch.equal(first, step.out)
+
+
+@pytest.mark.parametrize("scale", [-0.0721687836, 0.0, 0.5])
+def test_softmax_scale_sign_zero_and_large(scale):
+    """A negative scale, a zero scale (uniform weights over visible keys) and a large one."""
+    spec = workloads.Spec("scale", 2, (0, 0), (0, 0), 3, 16, True, "bf16", row_width=576, rope_col=512, seed=90)
+    w = workloads.build(spec, n=[150, 33], p=[20, 0])
+    w.softmax_scale = scale
+    step = _run(w)
+    bro, co, _ = check_plan(step, w)
+    ref = oracle_full(w, bro[0], co[0])
+    assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, f"scale{scale}") <= BAR_BF16
