@@ -236,15 +236,27 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     const int32_t j0 = kt * BN;
     if (wave_rows && c0 + j0 <= wq_last) {
       const uint8_t* st = lds + stage * STAGE;
+      // S^T = K Q^T.  K fragments go through a three-deep register ring, read two
+      // k-steps ahead of their MFMAs so LDS latency overlaps the MFMA chain; the
+      // scheduling barriers keep the compiler from sinking the reads to their uses.
       f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < 12; ++ks) {
+      bf16x8 kf[3][2];
+      auto kread = [&](int ks, bf16x8 (&dst)[2]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const uint32_t off = ks < 8 ? kn_rd[ks] + kb * 32 * 256 : kr_rd[ks - 8] + kb * 32 * 128;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + off);
-          s[kb] = mfma_bf16(ka, qop[ks], s[kb]);
+          dst[kb] = *reinterpret_cast<const bf16x8*>(st + off);
         }
+      };
+      kread(0, kf[0]);
+      kread(1, kf[1]);
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) {
+        if (ks + 2 < 12) kread(ks + 2, kf[(ks + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(kf[ks % 3][kb], qop[ks], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // s[kb][r] is key j0 + 32kb + 4hf + roff(r), roff(r) = 8(r/4) + r%4
       const bool full = (j0 + BN <= len) && (c0 + j0 + BN - 1 <= wq_first);
@@ -260,6 +272,18 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
           }
         }
       }
+      // first V fragments, read while the softmax runs
+      bf16x8 vf[2][4];
+      auto vread = [&](int kk, bf16x8 (&dst)[4]) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const MLA_LDS uint8_t* base = (const MLA_LDS uint8_t*)st + v_rd[d] + kk * 16 * 256;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base + 8 * 256));
+          dst[d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
+      vread(0, vf[0]);
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -294,20 +318,16 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         l_run += ps0 + ps1;
       }
 
-      // O^T += V^T P^T, four 16-key steps
+      // O^T += V^T P^T, four 16-key steps; V fragments are read one step ahead
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const i32x4 pv = {(int)pw[4 * kk], (int)pw[4 * kk + 1], (int)pw[4 * kk + 2], (int)pw[4 * kk + 3]};
         const bf16x8 pop = __builtin_bit_cast(bf16x8, pv);
+        if (kk + 1 < 4) vread(kk + 1, vf[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const MLA_LDS uint8_t* base = (const MLA_LDS uint8_t*)st + v_rd[d] + kk * 16 * 256;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base + 8 * 256));
-          typedef __attribute__((ext_vector_type(8))) short i16x8;
-          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[d] = mfma_bf16(__builtin_bit_cast(bf16x8, both), pop, o[d]);
-        }
+        for (int d = 0; d < 4; ++d) o[d] = mfma_bf16(vf[kk & 1][d], pop, o[d]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
