@@ -173,7 +173,7 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
     a.scale_log2 = c > 1e-30f ? c : 1e-30f;  // scale 0: every visible key weighs the same
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (fp8) return MLA_ERR_UNSUPPORTED_DTYPE;  // fp8 kernel not built yet
+  if (fp8) return hip_status(mla::launch_prefill_fp8(a, q_max, s));
   return hip_status(mla::launch_prefill_bf16(a, q_max, s));
 }
 

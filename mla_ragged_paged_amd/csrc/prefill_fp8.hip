@@ -1,0 +1,365 @@
+// Ragged, causally masked MLA prefill over a paged K_rope cache -- float8_e4m3fn
+// inputs with per-tensor fp32 scales, bf16 output, fp32 accumulation.
+// Semantics: page "flare_mla_prefill" (description; Parameters: q may be
+// float8_e4m3fn and the output is then bfloat16; the k_rope_scales overload);
+// every fp8 operand stands for code * scale of its tensor.
+//
+// Same work decomposition, LDS staging and online softmax as the bf16 kernel
+// (BM = 128 queries per workgroup of four waves, BN = 64 keys per tile, two
+// direct-to-LDS stages, S^T with one query per lane column); what differs:
+//   * S^T = K . Q^T runs on the fp8 32x32x64 MFMA: two k-steps over the 128
+//     nope columns, then one over the 64 rope columns.  The nope partial sum is
+//     multiplied by s_knope / s_krope before the rope step, and
+//     s_q * s_krope * |scale| * log2(e) is folded into the exp2 argument.
+//   * P.V on tiles every query of the wave fully sees runs on the same fp8
+//     MFMA: p (at most 2^RESCALE_LOG2) is rounded to e4m3 and the row sum is
+//     taken over the rounded values, so the weights stay exactly normalised.
+//     Tiles that straddle the causal diagonal or the end of the keys -- where a
+//     row has few keys and fp8 weights would be coarse -- use the bf16 MFMA with
+//     V converted exactly from e4m3 to bf16 and bf16 p.
+//   * V is read transposed with ds_read_b64_tr_b8 (8 keys of one dv column per
+//     lane); s_v is applied to O in the epilogue.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int BM = 128;            // queries per workgroup
+constexpr int BN = 64;             // keys per tile
+constexpr int NT = 256;            // threads per workgroup
+constexpr int DQK = 192, DNOPE = 128, DV = 128;
+constexpr float RESCALE_LOG2 = 8.0f;
+
+// LDS stage layout (bytes): rows of fp8, 16-byte chunks XOR-swizzled per row
+constexpr int KN_OFF = 0;                      // K_nope [64 rows][8 chunks]
+constexpr int KR_OFF = KN_OFF + BN * 128;      // K_rope [64 rows][4 chunks]
+constexpr int V_OFF = KR_OFF + BN * 64;        // V      [64 rows][8 chunks]
+constexpr int STAGE = V_OFF + BN * 128;        // 20 KiB
+
+__device__ __forceinline__ int swz_kn(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_kr(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_v(int r) { return 2 * (((r >> 1) & 1) | ((r >> 2) & 2)); }
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // e4m3 x e4m3 (format code 0 for both operands), unit block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ i32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, MLA_LDS void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+
+// four e4m3 bytes -> four bf16 (exact)
+__device__ __forceinline__ i32x2 e4m3x4_to_bf16x4(int x) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+  return i32x2{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
+
+  // ---- work unit (same XCD-aware, longest-first order as the bf16 kernel)
+  const uint32_t bid = blockIdx.x;
+  const uint32_t logical = (bid & 7u) * a.units_per_xcd + (bid >> 3);
+  if (logical >= a.units) return;
+  const uint32_t qt = a.qtiles - 1u - logical % a.qtiles;
+  const uint32_t hb = logical / a.qtiles;
+  const uint32_t b = hb % a.batch;
+  const uint32_t h = hb / a.batch;
+  const uint32_t t0 = a.valid_length[b];
+  const uint32_t n = a.valid_length[b + 1] - t0;
+  const uint32_t i0 = qt * BM;
+  if (i0 >= n) return;
+
+  const uint32_t H = a.heads;
+  const int32_t p = (int32_t)a.cache_lengths[b];
+  const uint32_t g0 = a.cache_row_offsets[b];
+  const int32_t len = (int32_t)(a.cache_row_offsets[b + 1] - g0);
+  const int32_t c0 = a.cache_offsets ? (int32_t)a.cache_offsets[b] : 0;
+  const int32_t i_last = (int32_t)min(n, i0 + BM) - 1;
+  const int32_t jend = max(0, min(p + i_last - c0 + 1, len));
+  const int32_t nkt = (jend + BN - 1) / BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int li = lane & 31, hf = lane >> 5;
+  const int32_t iw0 = (int32_t)i0 + 32 * w;
+  const bool wave_rows = iw0 < (int32_t)n;
+  const int32_t my_i = iw0 + li;
+  const int32_t wq_first = p + iw0;
+  const int32_t wq_last = p + min((int32_t)n, iw0 + 32) - 1;
+
+  // per-tensor dequantisation scales
+  const float s_q = *a.q_scale, s_kn = *a.k_nope_scale, s_v = *a.v_scale, s_kr = *a.k_rope_scale;
+
+  const uint32_t q_row = H * DQK, kv_row = H * DNOPE;
+  const auto q_rs = rsrc(static_cast<const uint8_t*>(a.q) + ((size_t)t0 * H + h) * DQK, (n - 1) * q_row + DQK);
+  const uint32_t kv_bytes = jend > 0 ? (uint32_t)(jend - 1) * kv_row + DNOPE : 0u;
+  const auto kn_rs = rsrc(static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE, kv_bytes);
+  const auto v_rs = rsrc(static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE, kv_bytes);
+  const auto cr_rs = rsrc(a.cache, a.cache_bytes);
+  const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
+  const uint32_t cache_row = a.row_width;
+
+  for (int k = tid; k < BN * 8; k += NT) {           // V stages start as zeros
+    *reinterpret_cast<i32x4*>(&stage0[V_OFF + 16 * k]) = i32x4{0, 0, 0, 0};
+    *reinterpret_cast<i32x4*>(&stage1[V_OFF + 16 * k]) = i32x4{0, 0, 0, 0};
+  }
+
+  // ---- Q^T operands: lane (li, hf) holds bytes [64ks + 32hf, +32) of its query
+  i32x8 qop[3];
+  {
+    const int sign = a.scale < 0.f ? (int)0x80808080 : 0;
+    const uint32_t qoff = (uint32_t)my_i * q_row + hf * 32;
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      const i32x4 x0 = bload16(q_rs, qoff + ks * 64) ^ sign;
+      const i32x4 x1 = bload16(q_rs, qoff + ks * 64 + 16) ^ sign;
+      qop[ks] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
+  }
+
+  // ---- this lane's slots of a tile load (one 1 KiB load = 64 slots of 16 B)
+  uint32_t kn_off[2], v_off[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {                      // K_nope / V load m = 2w + u: rows 8m .. 8m+7
+    const int r = 16 * w + 8 * u + (lane >> 3);
+    const int cs = lane & 7;
+    kn_off[u] = (uint32_t)r * kv_row + 16u * (uint32_t)(cs ^ swz_kn(r));
+    v_off[u] = (uint32_t)r * kv_row + 16u * (uint32_t)(cs ^ swz_v(r));
+  }
+  const int kr_row = 16 * w + (lane >> 2);           // K_rope load m = w: rows 16m .. 16m+15
+  const int kr_chunk = (lane & 3) ^ swz_kr(kr_row);
+  auto page_of = [&](int32_t kt) -> uint32_t {
+    const int32_t j = min(kt * BN + kr_row, jend - 1);
+    const uint32_t pos = (uint32_t)(c0 + j);
+    return a.page_shift < 32u ? PT[pos >> a.page_shift] : PT[pos / a.page_size];
+  };
+  auto issue_tile = [&](int32_t kt, uint8_t* stage, uint32_t pg) {
+    const uint32_t jrow = (uint32_t)(kt * BN) * kv_row;
+    MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)stage;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int m = 2 * w + u;
+      bload_lds(kn_rs, jrow + kn_off[u], st + KN_OFF + m * 1024);
+      bload_lds(v_rs, jrow + v_off[u], st + V_OFF + m * 1024);
+    }
+    const int32_t j = min(kt * BN + kr_row, jend - 1);
+    const uint32_t pos = (uint32_t)(c0 + j);
+    const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
+    bload_lds(cr_rs, (pg * a.page_size + slot) * cache_row + a.rope_col + 16u * kr_chunk, st + KR_OFF + w * 1024);
+  };
+
+  // ---- LDS read offsets.  K operand (fp8 32x32x64): row R = 32kb + li, bytes
+  // [64ks + 32hf, +32) = chunks 4ks + 2hf and +1 (nope), 2hf and +1 (rope).
+  uint32_t kn_rd[2][2], kr_rd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) kn_rd[ks][x] = KN_OFF + li * 128 + 16 * ((4 * ks + 2 * hf + x) ^ swz_kn(li));
+#pragma unroll
+  for (int x = 0; x < 2; ++x) kr_rd[x] = KR_OFF + li * 64 + 16 * ((2 * hf + x) ^ swz_kr(li));
+  // V transposed byte reads (ds_read_b64_tr_b8: lane 16g + 2e + c supplies row e,
+  // bytes 8c..8c+7; lane 16g + i receives column i of the 8 rows).  For 16-key
+  // step t: rows 16t + 4(g>>1) + (e&3) + 8(e>>2), dv = 32d + 16(g&1) + 8c.
+  const int tr_g = lane >> 4, tr_e = (lane >> 1) & 7, tr_c = lane & 1;
+  const int tr_row = 4 * (tr_g >> 1) + (tr_e & 3) + 8 * (tr_e >> 2);
+  // swz_v(r + 16t) == swz_v(r), so v_rd[d] + t * 16 * 128 addresses step t.
+  uint32_t v_rd[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int chunk = 2 * d + (tr_g & 1);
+    v_rd[d] = V_OFF + tr_row * 128 + 16 * (chunk ^ swz_v(tr_row)) + 8 * tr_c;
+  }
+
+  // ---- softmax state
+  const float c = a.scale_log2 * s_q * s_kr;         // exp2 factor for the combined score
+  const float ratio = s_kn / s_kr;                   // nope partial sum -> rope units
+  const float thr = RESCALE_LOG2 / c;
+  float m_run = -1e30f, mc = m_run * c, l_run = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = f32x16{};
+
+  uint32_t pg_next = 0u;
+  if (nkt > 0) {
+    const uint32_t pg0 = page_of(0);
+    __syncthreads();
+    issue_tile(0, stage0, pg0);
+    pg_next = page_of(1);
+  }
+
+  auto step = [&](int32_t kt, const uint8_t* st, uint8_t* next) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      issue_tile(kt + 1, next, pg_next);
+      pg_next = page_of(kt + 2);
+    }
+    const int32_t j0 = kt * BN;
+    if (!(wave_rows && c0 + j0 <= wq_last)) return;
+    // S^T: two nope k-steps, scale to rope units, one rope k-step
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      i32x8 kf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t o0 = ks < 2 ? kn_rd[ks][0] + kb * 32 * 128 : kr_rd[0] + kb * 32 * 64;
+        const uint32_t o1 = ks < 2 ? kn_rd[ks][1] + kb * 32 * 128 : kr_rd[1] + kb * 32 * 64;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(st + o0);
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(st + o1);
+        kf[kb] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+      if (ks == 2) {
+        s[0] *= ratio;
+        s[1] *= ratio;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_fp8(kf[kb], qop[ks], s[kb]);
+    }
+    const bool full = (j0 + BN <= len) && (c0 + j0 + BN - 1 <= wq_first);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int32_t kbase = j0 + 32 * kb + 4 * hf;
+        const int32_t lim = min(len - 1 - kbase, p + my_i - c0 - kbase);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t roff = 8 * (r >> 2) + (r & 3);
+          s[kb][r] = roff <= lim ? s[kb][r] : -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_across_halves(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      mc = m_run * c;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] *= alpha;
+    }
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float e[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+
+    if (full) {
+      // fp8 P: byte 16kb + r of this lane is key 32kb + 8(r/4) + 4hf + r%4
+      int pq[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int kb = x >> 2, r = 4 * (x & 3);
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r], e[kb][r + 1], 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r + 2], e[kb][r + 3], wd, true);
+        pq[x] = wd;
+      }
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, false), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, true), ones, ps1, false);
+      }
+      l_run += ps0 + ps1;
+      const i32x8 pop = {pq[0], pq[1], pq[2], pq[3], pq[4], pq[5], pq[6], pq[7]};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        int va[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (MLA_LDS i32x2*)((const MLA_LDS uint8_t*)st + v_rd[d] + t * 16 * 128));
+          va[2 * t] = v2[0];
+          va[2 * t + 1] = v2[1];
+        }
+        o[d] = mfma_fp8(i32x8{va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]}, pop, o[d]);
+      }
+    } else {
+      // bf16 P with V converted exactly from e4m3
+      uint32_t pw[16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) pw[8 * kb + x] = pack_bf16x2(e[kb][2 * x], e[kb][2 * x + 1]);
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; x += 2) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x]), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x + 1]), ones, ps1, false);
+      }
+      l_run += ps0 + ps1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i32x4 pv = {(int)pw[4 * t], (int)pw[4 * t + 1], (int)pw[4 * t + 2], (int)pw[4 * t + 3]};
+        const bf16x8 pop = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (MLA_LDS i32x2*)((const MLA_LDS uint8_t*)st + v_rd[d] + t * 16 * 128));
+          const i32x2 lo = e4m3x4_to_bf16x4(v2[0]), hi = e4m3x4_to_bf16x4(v2[1]);
+          const bf16x8 va = __builtin_bit_cast(bf16x8, i32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[d] = mfma_bf16(va, pop, o[d]);
+        }
+      }
+    }
+  };
+  for (int32_t kt = 0; kt < nkt; kt += 2) {
+    step(kt, stage0, stage1);
+    if (kt + 1 < nkt) step(kt + 1, stage1, stage0);
+  }
+
+  // ---- epilogue: row sums of both halves, normalise, apply s_v, round to bf16
+  const float l_tot = l_run + swap_halves(l_run);
+  const float inv = l_tot > 0.f ? s_v / l_tot : 0.f;
+  if (my_i < (int32_t)n) {
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(t0 + my_i) * H + h) * DV;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dv = d * 32 + g * 8 + hf * 4;
+        const uint32_t w0 = pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + dv) = u32x2{w0, w1};
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream) {
+  a.qtiles = (q_max + BM - 1) / BM;
+  const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles;
+  a.units = (uint32_t)units;
+  const uint64_t grid = (units + 7) / 8 * 8;
+  a.units_per_xcd = (uint32_t)(grid / 8);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_fp8_kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla
