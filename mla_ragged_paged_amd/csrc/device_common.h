@@ -40,4 +40,42 @@ __device__ __forceinline__ float max_across_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// One work unit of the prefill kernels: (head, sequence, 128-query tile).
+struct WorkUnit {
+  uint32_t h, b, qt;
+};
+
+// Maps a workgroup id to its work unit; false for ids past the last unit.
+// Workgroup ids go round-robin over the 8 XCDs (id % 8), and within an XCD
+// round-robin over its 4 shader engines ((id / 8) % 4), each of which starts
+// its workgroups in id order.  When H is a multiple of 8, XCD x takes heads
+// [x*H/8, (x+1)*H/8), so its L2 serves those heads' K/V.  Within an XCD a
+// sequence's tiles run longest-first; with several sequences the heads go in
+// quads, so the 4 consecutive ids that reach the 4 shader engines are the same
+// (sequence, tile) of 4 heads and cost the same (tiles past a short sequence's
+// end then fall evenly on all engines too).  With one sequence, neighbouring
+// tiles of one head already cost nearly the same and one head at a time keeps
+// the XCD's L2 on one K/V stream.  Other head counts: tiles longest-first, then
+// sequence, then head, over the whole chip.
+__device__ __forceinline__ bool decode_unit(uint32_t bid, uint32_t H, uint32_t B, uint32_t Q, WorkUnit& u) {
+  if (bid >= H * B * Q) return false;
+  if ((H & 7u) == 0) {
+    const uint32_t hx = H >> 3, xcd = bid & 7u, j = bid >> 3;
+    const uint32_t g = B > 1 ? 4u : 1u;
+    const uint32_t hs = j / (g * B * Q) * g;      // first head (within the XCD) of this group
+    const uint32_t gl = min(g, hx - hs);          // heads in this group
+    const uint32_t r = j - hs * B * Q;
+    const uint32_t bq = r / gl;
+    u.h = xcd * hx + hs + r % gl;
+    u.b = bq / Q;
+    u.qt = Q - 1u - bq % Q;
+  } else {
+    const uint32_t rest = bid / H;
+    u.h = bid % H;
+    u.b = rest % B;
+    u.qt = Q - 1u - rest / B;
+  }
+  return true;
+}
+
 }  // namespace mla

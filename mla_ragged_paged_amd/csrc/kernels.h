@@ -58,8 +58,6 @@ struct PrefillArgs {
   uint32_t batch;
   uint32_t heads;
   uint32_t qtiles;                    // query tiles per sequence (launch bound)
-  uint32_t units;                     // heads * batch * qtiles
-  uint32_t units_per_xcd;             // grid size / 8
   float scale;                        // softmax scale (its sign is applied to Q)
   float scale_log2;                   // max(|scale| * log2(e), 1e-30)
 };

@@ -73,14 +73,11 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
 
-  // ---- work unit (same XCD-aware, longest-first order as the bf16 kernel)
+  // ---- work unit (XCD- and shader-engine-aware order, longest tiles first)
   const uint32_t bid = blockIdx.x;
-  const uint32_t logical = (bid & 7u) * a.units_per_xcd + (bid >> 3);
-  if (logical >= a.units) return;
-  const uint32_t qt = a.qtiles - 1u - logical % a.qtiles;
-  const uint32_t hb = logical / a.qtiles;
-  const uint32_t b = hb % a.batch;
-  const uint32_t h = hb / a.batch;
+  WorkUnit u;
+  if (!decode_unit(bid, a.heads, a.batch, a.qtiles, u)) return;
+  const uint32_t h = u.h, b = u.b, qt = u.qt;
   const uint32_t t0 = a.valid_length[b];
   const uint32_t n = a.valid_length[b + 1] - t0;
   const uint32_t i0 = qt * BM;
@@ -354,9 +351,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
 hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream) {
   a.qtiles = (q_max + BM - 1) / BM;
   const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles;
-  a.units = (uint32_t)units;
   const uint64_t grid = (units + 7) / 8 * 8;
-  a.units_per_xcd = (uint32_t)(grid / 8);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_fp8_kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();

@@ -41,6 +41,9 @@ SMALL = [
     dict(n=[40, 7], p=[10, 3], heads=2, ps=1, width=64, rope=0),            # one token per page, rope-only rows
     dict(n=[1, 1, 2], p=[0, 9, 0], heads=5, ps=16, width=128, rope=64),     # single-token sequences
     dict(n=[513], p=[0], heads=2, ps=128, width=576, rope=512),             # 4 full tiles + 1 row
+    dict(n=[130, 40, 0, 200], p=[10, 0, 5, 64], heads=16, ps=16, width=576, rope=512),  # heads in groups per XCD
+    dict(n=[300], p=[20], heads=8, ps=64, width=576, rope=512),             # one sequence, one head per XCD
+    dict(n=[70, 150, 3], p=[0, 0, 9], heads=24, ps=32, width=576, rope=512),  # 3 heads per XCD: partial group
 ]
 
 
@@ -104,6 +107,10 @@ def test_full_size_workloads_sampled(name):
     say(f"{name}: B={w.batch} T={w.total_q} C={w.total_ctx} H={w.heads}")
     step = _run(w)
     bro, co, _ = check_plan(step, w)
+    # every (token, head) output is written by exactly the launch under test
+    step.out.fill_(float("nan"))
+    step.attention(0)
+    torch.cuda.synchronize()
     out = step.out.float()
     assert bool(torch.isfinite(out).all())
     rows = sample_rows(w, 160, seed=7)
