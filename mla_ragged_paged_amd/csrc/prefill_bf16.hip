@@ -116,25 +116,15 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
   const uint32_t cache_row = a.row_width * 2;
 
-  // ---- V stages start as zeros: rows past the keys are never NaN garbage
-  for (int i = tid; i < 2 * BN * 16; i += NT) {
-    const int s = i / (BN * 16), k = i % (BN * 16);
-    *reinterpret_cast<i32x4*>(&lds[s * STAGE + V_OFF + 16 * k]) = i32x4{0, 0, 0, 0};
-  }
-
   // ---- Q^T operands: lane (li, hf) holds q[t][h][16ks + 8hf .. +7] for its query
-  // (rows past the sequence read as zeros; a negative scale flips the sign of Q)
+  // (rows past the sequence read as zeros).  Loaded after the first tile's
+  // page ids and K_nope / V loads (vector-memory waits are in issue order).
   bf16x8 qop[12];
-  {
-    const int sign = a.scale < 0.f ? (int)0x80008000 : 0;
+  auto load_q = [&]() {
     const uint32_t qoff = (uint32_t)my_i * q_row + hf * 16;
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) {
-      i32x4 x = bload16(q_rs, qoff + ks * 32);
-      x ^= sign;
-      qop[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
+    for (int ks = 0; ks < 12; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, bload16(q_rs, qoff + ks * 32));
+  };
 
   // ---- this lane's slots of a tile load (one 1 KiB load = 64 slots of 16 B)
   // K_nope / V: load m = 4w + u covers rows 4m .. 4m+3, slot lane -> row 4m + lane/16,
@@ -160,7 +150,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     const uint32_t pos = (uint32_t)(c0 + j);
     return a.page_shift < 32u ? PT[pos >> a.page_shift] : PT[pos / a.page_size];
   };
-  auto issue_tile = [&](int32_t kt, int stage, const uint32_t (&pg)[2]) {
+  // K_nope and V rows of tile kt, then its K_rope rows (which need the page ids).
+  // Rows past the keys are filled with zeros by the range-checked loads, so no
+  // stage ever holds stale or uninitialised V rows.
+  auto issue_kv = [&](int32_t kt, int stage) {
     const uint32_t jrow = (uint32_t)(kt * BN) * kv_row;
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * STAGE;
 #pragma unroll
@@ -169,6 +162,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       bload_lds(kn_rs, jrow + kn_off[u], st + KN_OFF + m * 1024);
       bload_lds(v_rs, jrow + v_off[u], st + V_OFF + m * 1024);
     }
+  };
+  auto issue_rope = [&](int32_t kt, int stage, const uint32_t (&pg)[2]) {
+    MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * STAGE;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int m = 2 * w + u;
@@ -208,13 +204,22 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = f32x16{};
 
+  // ---- prologue, ordered for the first tile's critical path: page ids first,
+  // then the K_nope / V rows, then Q, so the K_rope loads wait for the page ids
+  // only; the sign of a negative scale is applied to Q once it has arrived.
   uint32_t pg_next[2] = {0u, 0u};
   if (nkt > 0) {
     const uint32_t pg0[2] = {page_of(0, 0), page_of(0, 1)};
-    __syncthreads();                                 // V zero-fill done before any load lands
-    issue_tile(0, 0, pg0);
     pg_next[0] = page_of(1, 0);
     pg_next[1] = page_of(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_kv(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_q();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_rope(0, 0, pg0);
+  } else {
+    load_q();
   }
 
   for (int32_t kt = 0; kt < nkt; ++kt) {
@@ -222,8 +227,14 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     // publish tile kt (every wave's loads done) and retire stage (kt+1)&1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (kt == 0 && a.scale < 0.f) {
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks)
+        qop[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(i32x4, qop[ks]) ^ (int)0x80008000);
+    }
     if (kt + 1 < nkt) {
-      issue_tile(kt + 1, stage ^ 1, pg_next);
+      issue_kv(kt + 1, stage ^ 1);
+      issue_rope(kt + 1, stage ^ 1, pg_next);
       pg_next[0] = page_of(kt + 2, 0);
       pg_next[1] = page_of(kt + 2, 1);
     }

@@ -113,23 +113,19 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
   const uint32_t cache_row = a.row_width;
 
-  for (int k = tid; k < BN * 8; k += NT) {           // V stages start as zeros
-    *reinterpret_cast<i32x4*>(&stage0[V_OFF + 16 * k]) = i32x4{0, 0, 0, 0};
-    *reinterpret_cast<i32x4*>(&stage1[V_OFF + 16 * k]) = i32x4{0, 0, 0, 0};
-  }
-
-  // ---- Q^T operands: lane (li, hf) holds bytes [64ks + 32hf, +32) of its query
+  // ---- Q^T operands: lane (li, hf) holds bytes [64ks + 32hf, +32) of its query.
+  // Loaded after the first tile's page ids and K_nope / V loads (vector-memory
+  // waits are in issue order); a negative scale's sign is applied once Q is in.
   i32x8 qop[3];
-  {
-    const int sign = a.scale < 0.f ? (int)0x80808080 : 0;
+  auto load_q = [&]() {
     const uint32_t qoff = (uint32_t)my_i * q_row + hf * 32;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
-      const i32x4 x0 = bload16(q_rs, qoff + ks * 64) ^ sign;
-      const i32x4 x1 = bload16(q_rs, qoff + ks * 64 + 16) ^ sign;
+      const i32x4 x0 = bload16(q_rs, qoff + ks * 64);
+      const i32x4 x1 = bload16(q_rs, qoff + ks * 64 + 16);
       qop[ks] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
-  }
+  };
 
   // ---- this lane's slots of a tile load (one 1 KiB load = 64 slots of 16 B)
   uint32_t kn_off[2], v_off[2];
@@ -147,7 +143,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
     const uint32_t pos = (uint32_t)(c0 + j);
     return a.page_shift < 32u ? PT[pos >> a.page_shift] : PT[pos / a.page_size];
   };
-  auto issue_tile = [&](int32_t kt, uint8_t* stage, uint32_t pg) {
+  // K_nope and V rows of tile kt, then its K_rope rows (which need the page id).
+  // Rows past the keys are filled with zeros by the range-checked loads, so no
+  // stage ever holds stale or uninitialised V rows.
+  auto issue_kv = [&](int32_t kt, uint8_t* stage) {
     const uint32_t jrow = (uint32_t)(kt * BN) * kv_row;
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)stage;
 #pragma unroll
@@ -156,6 +155,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       bload_lds(kn_rs, jrow + kn_off[u], st + KN_OFF + m * 1024);
       bload_lds(v_rs, jrow + v_off[u], st + V_OFF + m * 1024);
     }
+  };
+  auto issue_rope = [&](int32_t kt, uint8_t* stage, uint32_t pg) {
+    MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)stage;
     const int32_t j = min(kt * BN + kr_row, jend - 1);
     const uint32_t pos = (uint32_t)(c0 + j);
     const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
@@ -193,19 +195,32 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = f32x16{};
 
+  // ---- prologue, ordered for the first tile's critical path: page ids first,
+  // then the K_nope / V rows, then Q, so the K_rope loads wait for the page ids only
   uint32_t pg_next = 0u;
   if (nkt > 0) {
     const uint32_t pg0 = page_of(0);
-    __syncthreads();
-    issue_tile(0, stage0, pg0);
     pg_next = page_of(1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_kv(0, stage0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_q();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_rope(0, stage0, pg0);
+  } else {
+    load_q();
   }
 
   auto step = [&](int32_t kt, const uint8_t* st, uint8_t* next) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (kt == 0 && a.scale < 0.f) {
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) qop[ks] ^= (int)0x80808080;
+    }
     if (kt + 1 < nkt) {
-      issue_tile(kt + 1, next, pg_next);
+      issue_kv(kt + 1, next);
+      issue_rope(kt + 1, next, pg_next);
       pg_next = page_of(kt + 2);
     }
     const int32_t j0 = kt * BN;
