@@ -13,6 +13,10 @@ roofline = the attention kernel (the dominant one): algorithmic FLOPs per launch
            against the MI355X dense MFMA peak of the compute dtype.
 cpu_baseline = the float64 oracle timed on the host on a bounded sample of the
            same workload (a subset of heads), scaled to TFLOP/s.
+Also reported: plan / gather / attention times (mean, median, min over the timed
+steps), the attention time with L2 and MALL flushed by a 512 MiB write before
+each launch (cold_cache), and the gather kernel's bandwidth on a >= 1 GiB
+paged cache of 576-wide bf16 rows (gather_bench).
 """
 from __future__ import annotations
 
@@ -67,9 +71,12 @@ def cpu_baseline(w, budget_s: float):
 
     import oracle
     from mla_ragged_paged_amd import workloads
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+        info = threadpool_info()
+        threads = max([int(i.get("num_threads", 1)) for i in info] + [1])
+        blas = [f"{i.get('internal_api', '?')}:{i.get('num_threads', '?')}" for i in info]
     except Exception:  # pragma: no cover
         threads = 1
     q, kn, v = w.q, w.k_nope, w.v
@@ -85,19 +92,74 @@ def cpu_baseline(w, budget_s: float):
         heads += 1
     dt = time.perf_counter() - t0
     flops = workloads.causal_flops(w.n, w.p, heads)
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"float64 numpy oracle, heads 0..{heads - 1} of {w.heads} (all {w.batch} sequences), "
-                      f"{dt:.1f} s wall on the host, {threads} BLAS threads"}
+                      f"{dt:.1f} s wall on the host, {threads} BLAS threads; elementwise softmax single-threaded",
+            "cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas": blas}
+
+
+def gather_bench(torch, batch=64, n_range=(8192, 24576), width=576, page_size=128, seed=11, reps=5):
+    """Bandwidth of the gather kernel on a large paged cache (>= 1 GiB of 576-wide bf16
+    rows, shuffled physical pages): median over `reps` launches, bytes read + written."""
+    import numpy as np
+
+    from mla_ragged_paged_amd import _binding as B
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(seed)
+    L = rng.integers(n_range[0], n_range[1] + 1, size=batch)
+    pages = (L + page_size - 1) // page_size
+    num_pages = int(pages.sum())
+    perm = rng.permutation(num_pages)
+    table = np.zeros((batch, int(pages.max())), dtype=np.int64)
+    k = 0
+    for b in range(batch):
+        table[b, :pages[b]] = perm[k:k + pages[b]]
+        k += int(pages[b])
+    C = int(L.sum())
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    cache = torch.randn((1, num_pages, page_size, 1, width), generator=gen, device=dev).to(torch.bfloat16)
+    page_table = torch.from_numpy(table).to(torch.int32).to(dev)
+    zeros = torch.zeros(batch, dtype=torch.int32, device=dev)
+    iro = torch.from_numpy(np.concatenate([[0], np.cumsum(L)])).to(torch.int32).to(dev)
+    kv = B.PagedCache(cache, page_table, zeros, width - 64)
+    bro = torch.zeros(batch + 1, dtype=torch.int32, device=dev)
+    co = torch.zeros(batch, dtype=torch.int32, device=dev)
+    bl = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((C, width), dtype=torch.bfloat16, device=dev)
+    B.mla_prefill_plan(iro, kv, 0, C, bro.view(1, -1), co.view(1, -1), bl, None, None)
+    for _ in range(2):
+        B.mla_prefill_gather(kv, 0, bro, co, 0, width, out, None)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        B.mla_prefill_gather(kv, 0, bro, co, 0, width, out, None)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    # spot check: sampled rows equal the cache rows the page table names (exact copy)
+    rows = torch.from_numpy(rng.integers(0, C, size=256)).to(dev)
+    starts = torch.from_numpy(np.concatenate([[0], np.cumsum(L)[:-1]])).to(dev)
+    b_of = torch.searchsorted(starts, rows, right=True) - 1
+    pos = rows - starts[b_of]
+    ref = cache[0, page_table[b_of, pos // page_size].long(), pos % page_size, 0, :]
+    exact = bool(torch.equal(ref, out[rows]))
+    moved = 2.0 * C * width * 2
+    med = ms[len(ms) // 2]
+    return {"tokens": C, "row_bytes": width * 2, "page_size": page_size, "bytes_moved": moved,
+            "median_ms": round(med, 4), "min_ms": round(ms[0], 4), "GBps": round(moved / (med * 1e-3) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * moved / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 1), "sample_rows_exact": exact}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-extras", action="store_true", help="skip the cold-cache and gather-bandwidth measurements")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (scales HBM byte counters)")
     args = ap.parse_args()
@@ -151,8 +213,10 @@ def main():
     ms_step = wall * 1e3 / args.steps
     plan_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     gather_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
-    attn_best = min(e[2].elapsed_time(e[3]) for e in ev)
+    attn_all = sorted(e[2].elapsed_time(e[3]) for e in ev)
+    attn_ms = sum(attn_all) / args.steps
+    attn_best = attn_all[0]
+    attn_median = attn_all[len(attn_all) // 2]
 
     dtype = spec.dtype
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -180,7 +244,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic},
         "stages_ms": {"plan": round(plan_ms, 4), "gather": round(gather_ms, 4), "attention": round(attn_ms, 4),
-                      "attention_best": round(attn_best, 4)},
+                      "attention_median": round(attn_median, 4), "attention_best": round(attn_best, 4)},
         "pct_of_bf16_peak": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 2),
         "gather_GBps": round(gather_bytes / (gather_ms * 1e-3) / 1e9, 1),
         "causal_tflop_per_step": round(flops / 1e12, 5),
@@ -188,6 +252,25 @@ def main():
     }
     if dtype == "fp8":
         result["pct_of_fp8_peak"] = round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 2)
+    if not args.no_extras:
+        # attention with L2 and MALL flushed by a 512 MiB write before each launch
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        cold = []
+        for _ in range(7):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step.attention(0)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+        cold.sort()
+        result["cold_cache"] = {"flush_mib": 512, "attention_median_ms": round(cold[len(cold) // 2], 4),
+                                "attention_min_ms": round(cold[0], 4),
+                                "achieved_TFLOPs_median": round(flops / (cold[len(cold) // 2] * 1e-3) / 1e12, 2)}
+        print("[bench] gather bandwidth on a >= 1 GiB paged cache", file=sys.stderr, flush=True)
+        result["gather_bench"] = gather_bench(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

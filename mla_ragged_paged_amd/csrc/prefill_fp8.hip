@@ -201,6 +201,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   if (nkt > 0) {
     const uint32_t pg0 = page_of(0);
     pg_next = page_of(1);
+    // all four waves start their first tile together
+    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     issue_kv(0, stage0);
     __builtin_amdgcn_sched_barrier(0);
