@@ -65,7 +65,84 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   }
 }
 
-// One thread per copy unit (UNIT bytes) of a buffer slot; consecutive threads
+// Gather of wide rows (>= 32 copy units): each wave copies whole buffer slots,
+// GATHER_ROWS of them per step.  A slot's
+// sequence (binary search of the row's slice starts), cache position and
+// physical page are found once per slot in scalar registers; the 64 lanes then
+// walk the slot in UNIT-byte pieces, with all of the step's loads in flight
+// before its stores.
+template <typename T>
+__device__ __forceinline__ T ld_unit(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
+template <typename T>
+__device__ __forceinline__ void st_unit(uint8_t* p, T v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));   // streamed: the buffer is not re-read here
+}
+template <int UNIT> struct UnitType;
+template <> struct UnitType<16> { typedef i32x4 T; };
+template <> struct UnitType<8> { typedef uint64_t T; };
+template <> struct UnitType<4> { typedef uint32_t T; };
+template <> struct UnitType<2> { typedef uint16_t T; };
+template <> struct UnitType<1> { typedef uint8_t T; };
+
+constexpr int GATHER_ROWS = 8;
+
+template <int UNIT>
+__global__ void __launch_bounds__(256) gather_rows_kernel(GatherArgs a) {
+  typedef typename UnitType<UNIT>::T T;
+  extern __shared__ uint32_t bro[];           // [B + 1] slice starts of this row
+  const uint32_t B = a.batch;
+  for (uint32_t b = threadIdx.x; b <= B; b += 256) bro[b] = a.buffer_row_offsets[b];
+  __syncthreads();
+  // page table and cache offsets through the constant address space: the
+  // per-slot lookups are uniform, so they become scalar loads
+  typedef const __attribute__((address_space(4))) uint32_t CU32;
+  CU32* const PT = (CU32*)a.page_table;
+  CU32* const CO = (CU32*)a.cache_offsets;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t nwaves = gridDim.x * 4u;
+  const uint32_t first = __builtin_amdgcn_readfirstlane(bro[0]);
+  const uint32_t total = __builtin_amdgcn_readfirstlane(bro[B]);
+  const uint32_t upr = (uint32_t)(a.copy_bytes / UNIT);
+  for (uint32_t s0 = first + wave * GATHER_ROWS; s0 < total; s0 += nwaves * GATHER_ROWS) {
+    const uint8_t* src[GATHER_ROWS];
+    uint8_t* dst[GATHER_ROWS];
+    bool ok[GATHER_ROWS];
+    // sequence of the step's first slot: last b with bro[b] <= slot (binary search),
+    // then walk forward for the following slots
+    uint32_t lo = 0, hi = B;                  // invariant: bro[lo] <= s0 < bro[hi]
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(bro[mid]) <= s0) lo = mid; else hi = mid;
+    }
+    uint32_t next_start = __builtin_amdgcn_readfirstlane(bro[lo + 1]);
+#pragma unroll
+    for (int r = 0; r < GATHER_ROWS; ++r) {
+      const uint32_t slot = s0 + r;
+      ok[r] = slot < total;
+      while (ok[r] && slot >= next_start) {
+        ++lo;
+        next_start = __builtin_amdgcn_readfirstlane(bro[lo + 1]);
+      }
+      const uint32_t pos = CO[lo] + (slot - __builtin_amdgcn_readfirstlane(bro[lo]));
+      const uint32_t page = PT[(size_t)lo * a.max_pages + pos / a.page_size];
+      const size_t row = (size_t)page * a.page_size + pos % a.page_size;
+      src[r] = a.cache + row * a.row_bytes + a.col_bytes;
+      dst[r] = a.out + (size_t)slot * a.copy_bytes;
+    }
+    for (uint32_t c = lane; c < upr; c += 64u) {
+      T v[GATHER_ROWS];
+#pragma unroll
+      for (int r = 0; r < GATHER_ROWS; ++r)
+        if (ok[r]) v[r] = ld_unit<T>(src[r] + (size_t)c * UNIT);
+#pragma unroll
+      for (int r = 0; r < GATHER_ROWS; ++r)
+        if (ok[r]) st_unit<T>(dst[r] + (size_t)c * UNIT, v[r]);
+    }
+  }
+}
+
+// Gather of narrow rows: one thread per copy unit (UNIT bytes) of a buffer slot; consecutive threads
 // walk along a row so both the page read and the buffer write are coalesced.
 template <int UNIT>
 __global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
@@ -110,11 +187,25 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_gather(const GatherArgs& a, int unit, hipStream_t stream) {
+  const size_t lds = sizeof(uint32_t) * (a.batch + 1);
+  if (a.copy_bytes / unit >= 32) {                     // wide rows: a wave per slot
+    const uint64_t waves = ((uint64_t)a.cap + GATHER_ROWS - 1) / GATHER_ROWS;
+    uint64_t blocks = (waves + 3) / 4;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) blocks = 1;
+    switch (unit) {
+      case 16: hipLaunchKernelGGL(gather_rows_kernel<16>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+      case 8: hipLaunchKernelGGL(gather_rows_kernel<8>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+      case 4: hipLaunchKernelGGL(gather_rows_kernel<4>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+      case 2: hipLaunchKernelGGL(gather_rows_kernel<2>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+      default: hipLaunchKernelGGL(gather_rows_kernel<1>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
+    }
+    return hipGetLastError();
+  }
   const uint64_t units = (uint64_t)a.cap * (a.copy_bytes / unit);
   uint64_t blocks = (units + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks == 0) blocks = 1;
-  const size_t lds = sizeof(uint32_t) * (a.batch + 1);
   switch (unit) {
     case 16: hipLaunchKernelGGL(gather_kernel<16>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;
     case 8: hipLaunchKernelGGL(gather_kernel<8>, dim3((uint32_t)blocks), dim3(256), lds, stream, a); break;

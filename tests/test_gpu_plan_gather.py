@@ -29,11 +29,15 @@ def test_plan_and_gather_on_workloads(name):
     assert np.array_equal(got.cpu().numpy().astype(np.int64), ref)
 
 
+# narrow copies (a thread per 16-byte unit) and wide ones (>= 32 units: a wave per slot)
 ADVERSARIAL = [
     dict(n=[5, 0, 9, 1], p=[3, 7, 0, 0], cap=4),       # many rows, an empty sequence, straddling rows
     dict(n=[1, 1, 1], p=[0, 0, 0], cap=1),             # capacity one
     dict(n=[40, 3], p=[100, 17], cap=37),              # prefix split over rows
     dict(n=[0, 0], p=[0, 0], cap=8),                   # nothing at all
+    dict(n=[5, 0, 9, 1], p=[3, 7, 0, 0], cap=4, width=576, cols=(0, 576), ps=16),     # wide rows, 16-byte units
+    dict(n=[40, 0, 3, 70], p=[100, 0, 17, 5], cap=37, width=576, cols=(4, 300), ps=8),  # wide, 8-byte units
+    dict(n=[130, 1], p=[0, 200], cap=331, width=320, cols=(0, 320), ps=3),            # wide, one row, odd pages
 ]
 
 
@@ -41,10 +45,12 @@ ADVERSARIAL = [
 def test_plan_and_gather_adversarial(case):
     kw = ADVERSARIAL[case]
     say(f"plan+gather adversarial {kw}")
-    spec = workloads.Spec("adv", len(kw["n"]), (0, 0), (0, 0), 2, 4, True, "bf16", row_width=96, rope_col=32,
-                          seed=50 + case)
+    width = kw.get("width", 96)
+    cols = kw.get("cols", (8, 40))
+    spec = workloads.Spec("adv", len(kw["n"]), (0, 0), (0, 0), 2, kw.get("ps", 4), True, "bf16", row_width=width,
+                          rope_col=width - 64, seed=50 + case)
     w = workloads.build(spec, n=kw["n"], p=kw["p"])
-    step = PrefillStep(w, "cuda", cap=kw["cap"], gather_cols=(8, 40))
+    step = PrefillStep(w, "cuda", cap=kw["cap"], gather_cols=cols)
     step.plan()
     torch.cuda.synchronize()
     bro, co, bl = check_plan(step, w)
@@ -53,11 +59,11 @@ def test_plan_and_gather_adversarial(case):
         step.gathered.fill_(-3)
         step.gather(r)
         torch.cuda.synchronize()
-        init = np.full((step.cap, 40), -3, dtype=np.int64)
+        init = np.full((step.cap, cols[1]), -3, dtype=np.int64)
         # -3 as bf16 bits: compare raw 16-bit patterns
         fill_bits = int(torch.tensor([-3.0]).to(torch.bfloat16).view(torch.int16)[0])
         init[:] = fill_bits
-        ref = oracle.gather(bits, 0, w.page_table, w.spec.page_size, bro[r], co[r], 8, 40, init)
+        ref = oracle.gather(bits, 0, w.page_table, w.spec.page_size, bro[r], co[r], cols[0], cols[1], init)
         got = step.gathered.view(torch.int16).cpu().numpy().astype(np.int64)
         assert np.array_equal(got, ref), f"row {r}"
 
