@@ -35,13 +35,14 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}      # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(dtype: str = "bf16") -> str:
+    """Hash of the attention kernel sources of one dtype (its .hip file and the shared headers):
+    a committed traffic summary is used only when it was taken on these sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mla_ragged_paged_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in sorted([f"prefill_{dtype}.hip", "device_common.h", "kernels.h"]):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
@@ -221,7 +222,7 @@ def main():
     dtype = spec.dtype
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    khash = kernel_source_hash()
+    khash = kernel_source_hash(dtype)
     traffic = traffic_from_profiles(spec.name, khash)
     el = 1 if dtype == "fp8" else 2
     gather_bytes = 2.0 * w.total_ctx * w.cache.shape[4] * el
