@@ -1,4 +1,4 @@
-"""Parity oracle for ragged, causally masked MLA prefill over a paged KV cache.
+"""Parity oracle for ragged, masked (causal or null) MLA prefill over a paged KV cache.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link anything in this package: only the test-suite, the smoke check in
@@ -22,4 +22,6 @@ from .mla_oracle import (  # noqa: F401
     rope_rows,
     mla_prefill_ragged,
     mla_prefill_rows,
+    merge_partials,
+    MASKS,
 )

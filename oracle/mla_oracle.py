@@ -12,8 +12,13 @@ Sources, all Modular MAX API documentation pages:
   columns of K taken from the cache and shared by every head, the reduced
   output depth, ragged valid lengths) and Args section (valid_length,
   cache_row_offsets, cache_offsets, scale, output dtype).
-* "mla_prefill_v2_ragged" -- Args section (the causal mask predicate, the
-  softmax scale, start position taken from the cache length).
+* "mla_prefill_v2_ragged" -- Args section (the mask predicate -- causal,
+  null and others -- the softmax scale, start position taken from the cache
+  length).
+* "generic_flare_mla_prefill_ragged_paged_plan" again for several buffer
+  rows: each row holds part of the keys, so a row's attention is a partial
+  softmax; its log-sum-exp and the combine of partials (``merge_partials``)
+  make the rows add up to the attention over every key.
 
 Where the pages leave a step open the plain reading is taken; each such
 reading is named in the docstring of the function that relies on it
@@ -34,8 +39,10 @@ __all__ = [
     "plan",
     "gather",
     "rope_rows",
+    "MASKS",
     "mla_prefill_ragged",
     "mla_prefill_rows",
+    "merge_partials",
 ]
 
 NOPE_DEPTH = 128  # per-head K/V depth for DeepSeek V2/3 ("flare_mla_prefill", description)
@@ -189,13 +196,24 @@ def gather(cache, layer_idx: int, page_table, page_size: int, buffer_row_offsets
 # ---------------------------------------------------------------------------
 # Attention -- "flare_mla_prefill" and "mla_prefill_v2_ragged".
 # ---------------------------------------------------------------------------
-def _visible(qpos, kpos):
-    """Causal mask [n, m]: key j is visible to query i iff kpos[j] <= qpos[i].
+MASKS = ("causal", "null")
 
-    "mla_prefill_v2_ragged", Args (mask_functor): the mask is a causal
-    predicate; reading R-e makes the diagonal inclusive (a token sees itself).
+
+def _visible(qpos, kpos, mask="causal"):
+    """Mask [n, m]: is key j visible to query i?
+
+    "mla_prefill_v2_ragged", Args (mask_t, mask_functor): the mask is a
+    predicate chosen per call, causal or null among others.
+      causal  kpos[j] <= qpos[i]; reading R-e makes the diagonal inclusive
+              (a token sees itself).
+      null    every key the buffer row holds for the sequence is visible,
+              whatever the positions (reading R-s).
     """
-    return kpos[None, :] <= qpos[:, None]
+    if mask == "causal":
+        return kpos[None, :] <= qpos[:, None]
+    if mask == "null":
+        return np.ones((qpos.shape[0], kpos.shape[0]), dtype=bool)
+    raise ValueError(f"unknown mask {mask!r}")
 
 
 def _query_positions(cache_lengths, b, count):
@@ -217,8 +235,8 @@ def _key_positions(cache_offsets, b, count):
     return c0 + np.arange(count, dtype=np.int64)
 
 
-def _attend(q_rows, k_nope, k_rope, v, scale, qpos, kpos):
-    """Causal softmax attention of query rows over one key set, float64.
+def _attend(q_rows, k_nope, k_rope, v, scale, qpos, kpos, mask="causal"):
+    """Masked softmax attention of query rows over one key set, float64.
 
     q_rows [n, 192] (columns 0..127 nope, 128..191 rope: reading R-a);
     k_nope [m, 128] (this head); k_rope [m, 64] (shared by every head);
@@ -226,17 +244,21 @@ def _attend(q_rows, k_nope, k_rope, v, scale, qpos, kpos):
 
     score = scale * (q_nope . k_nope + q_rope . k_rope)   (scale multiplies
     the whole product: "flare_mla_prefill" Args, scale; reading R-f);
-    key j is visible to query i iff kpos[j] <= qpos[i]    (causal, inclusive
-    diagonal: reading R-e); output = softmax over visible keys applied to v;
-    a query with no visible key gets 0 (reading R-i).
+    visibility from ``_visible`` (causal: readings R-e; null: R-s);
+    output = softmax over visible keys applied to v; a query with no
+    visible key gets 0 (reading R-i).
+
+    Returns (out [n, 128], lse [n]) where lse = ln(sum over visible keys of
+    exp(score)), -inf for a query with no visible key (reading R-u).
     """
     n = q_rows.shape[0]
     out = np.zeros((n, v.shape[1]), dtype=np.float64)
+    lse = np.full(n, -np.inf, dtype=np.float64)
     if n == 0 or k_nope.shape[0] == 0:
-        return out
+        return out, lse
     s = q_rows[:, :NOPE_DEPTH] @ k_nope.T + q_rows[:, NOPE_DEPTH:] @ k_rope.T
     s = s * np.float64(scale)
-    visible = _visible(qpos, kpos)
+    visible = _visible(qpos, kpos, mask)
     s = np.where(visible, s, -np.inf)
     has_key = visible.any(axis=1)
     m = np.where(has_key, s.max(axis=1, initial=-np.inf), 0.0)
@@ -244,7 +266,32 @@ def _attend(q_rows, k_nope, k_rope, v, scale, qpos, kpos):
     denom = w.sum(axis=1)
     num = w @ v
     out[has_key] = num[has_key] / denom[has_key, None]
-    return out
+    lse[has_key] = m[has_key] + np.log(denom[has_key])
+    return out, lse
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Combine two partial attentions over disjoint key sets, float64.
+
+    Each partial is (o, lse): the softmax-weighted mean of its keys' values
+    and the log-sum-exp of its keys' scores, as ``_attend`` returns them.
+    Softmax over the union weights every key by exp(score - lse) with
+    lse = ln(exp(lse_a) + exp(lse_b)), so the union's output is
+    exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b (reading R-v).  Where
+    both sides saw no key (lse -inf on both), the result is 0 with lse -inf
+    (reading R-i).  o_* [..., D], lse_* [...]; returns (o, lse).
+    """
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    lse = np.logaddexp(lse_a, lse_b)
+    some = np.isfinite(lse)
+    safe = np.where(some, lse, 0.0)
+    wa = np.where(some, np.exp(lse_a - safe), 0.0)
+    wb = np.where(some, np.exp(lse_b - safe), 0.0)
+    o = wa[..., None] * o_a + wb[..., None] * o_b
+    return o, lse
 
 
 def _as_f64(x, scale=None):
@@ -263,13 +310,14 @@ def _sequence_keys(b, cache_row_offsets):
 
 def mla_prefill_rows(rows, q, k_nope, v, cache, layer_idx, page_table, page_size, rope_col,
                      cache_lengths, valid_length, cache_row_offsets, cache_offsets, scale,
-                     scales=None):
+                     scales=None, mask="causal", return_lse=False):
     """Output of selected (token, head) pairs, float64 [len(rows), 128].
 
     ``rows`` is a list of (t, h).  Same definition as ``mla_prefill_ragged``
     evaluated one output row at a time (used to check large problems on a
     sample of outputs).  ``scales`` = dict(q=, k_nope=, v=, k_rope=) when the
-    inputs are fp8 codes (reading R-l), else None.
+    inputs are fp8 codes (reading R-l), else None.  With ``return_lse`` the
+    log-sum-exp of each pair is returned too, (out, lse [len(rows)]).
     """
     sc = scales or {}
     fp8 = scales is not None
@@ -279,6 +327,7 @@ def mla_prefill_rows(rows, q, k_nope, v, cache, layer_idx, page_table, page_size
     p = np.asarray(cache_lengths, dtype=np.int64)
     B = vl.shape[0] - 1
     out = np.zeros((len(rows), NOPE_DEPTH), dtype=np.float64)
+    lse = np.full(len(rows), -np.inf, dtype=np.float64)
     for idx, (t, h) in enumerate(rows):
         b = int(np.searchsorted(vl, t, side="right") - 1)
         assert 0 <= b < B and vl[b] <= t < vl[b + 1]
@@ -291,8 +340,9 @@ def mla_prefill_rows(rows, q, k_nope, v, cache, layer_idx, page_table, page_size
         vv = _as_f64(v[g0:g0 + count, h, :], sc.get("v") if fp8 else None)
         kr_codes = rope_rows(cache, layer_idx, page_table, page_size, rope_col, b, kpos)
         kr = _as_f64(kr_codes, sc.get("k_rope") if fp8 else None)
-        out[idx] = _attend(qrow, kn, kr, vv, scale, qpos, kpos)[0]
-    return out
+        o1, l1 = _attend(qrow, kn, kr, vv, scale, qpos, kpos, mask)
+        out[idx], lse[idx] = o1[0], l1[0]
+    return (out, lse) if return_lse else out
 
 
 def rope_rows(cache, layer_idx, page_table, page_size, rope_col, b, positions):
@@ -315,7 +365,7 @@ def rope_rows(cache, layer_idx, page_table, page_size, rope_col, b, positions):
 
 def mla_prefill_ragged(q, k_nope, v, cache, layer_idx, page_table, page_size, rope_col,
                        cache_lengths, valid_length, cache_row_offsets, cache_offsets, scale,
-                       scales=None, q_block=512):
+                       scales=None, q_block=512, mask="causal", return_lse=False):
     """Full output [T, H, 128] float64 of one ragged MLA prefill call.
 
     Shapes ("flare_mla_prefill", description and Args):
@@ -330,6 +380,9 @@ def mla_prefill_ragged(q, k_nope, v, cache, layer_idx, page_table, page_size, ro
       cache_offsets[b]+j (0 when cache_offsets is None: a contiguous cache).
     ``scales`` (fp8 inputs, reading R-l): dict(q=, k_nope=, v=, k_rope=) of
     per-tensor fp32 scales; the inputs are then uint8/float8 codes.
+    ``mask`` is "causal" or "null" (``_visible``).  With ``return_lse``
+    returns (out, lse [T, H]), the log-sum-exp of each (token, head) over the
+    keys this call sees (reading R-u).
     Query rows are processed in blocks of ``q_block`` only to bound memory;
     every output row is computed exactly as its definition states.
     """
@@ -342,6 +395,7 @@ def mla_prefill_ragged(q, k_nope, v, cache, layer_idx, page_table, page_size, ro
     B = vl.shape[0] - 1
     T, H = int(q.shape[0]), int(q.shape[1])
     out = np.zeros((T, H, NOPE_DEPTH), dtype=np.float64)
+    lse = np.full((T, H), -np.inf, dtype=np.float64)
     for b in range(B):
         t0, t1 = int(vl[b]), int(vl[b + 1])
         if t1 == t0:
@@ -357,5 +411,6 @@ def mla_prefill_ragged(q, k_nope, v, cache, layer_idx, page_table, page_size, ro
             for s0 in range(t0, t1, q_block):
                 s1 = min(s0 + q_block, t1)
                 qb = _as_f64(q[s0:s1, h, :], sc.get("q") if fp8 else None)
-                out[s0:s1, h, :] = _attend(qb, kn, kr, vv, scale, qpos_all[s0 - t0:s1 - t0], kpos)
-    return out
+                out[s0:s1, h, :], lse[s0:s1, h] = _attend(qb, kn, kr, vv, scale,
+                                                          qpos_all[s0 - t0:s1 - t0], kpos, mask)
+    return (out, lse) if return_lse else out

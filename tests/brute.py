@@ -42,16 +42,20 @@ def plan_by_enumeration(input_row_offsets, cache_lengths, cap, rows):
     return bro, co, bl, (1 if used > rows else 0)
 
 
-def attention_brute(q, k_nope, v, rope, cache_lengths, valid_length, cache_row_offsets, cache_offsets, scale):
-    """out[t][h][d] by explicit loops.
+def attention_brute(q, k_nope, v, rope, cache_lengths, valid_length, cache_row_offsets, cache_offsets, scale,
+                    causal=True, with_lse=False):
+    """out[t][h][d] by explicit loops (and lse[t][h] with ``with_lse``).
 
     q[t][h][192], k_nope[g][h][128], v[g][h][128] nested lists of floats;
     rope(b, pos) -> list of 64 floats (the shared K_rope row of that cache position).
+    ``causal`` False takes every key of the sequence (the null mask).
+    lse = log of the sum of exp(score) over the keys taken, -inf if none.
     """
     B = len(valid_length) - 1
     T = len(q)
     H = len(q[0]) if T else 0
     out = [[[0.0] * 128 for _ in range(H)] for _ in range(T)]
+    lse = [[-math.inf] * H for _ in range(T)]
     for b in range(B):
         g0 = cache_row_offsets[b]
         m = cache_row_offsets[b + 1] - g0
@@ -63,7 +67,7 @@ def attention_brute(q, k_nope, v, rope, cache_lengths, valid_length, cache_row_o
                 scores = []
                 for j in range(m):
                     kpos = c0 + j
-                    if kpos > qpos:
+                    if causal and kpos > qpos:
                         continue
                     kr = rope(b, kpos)
                     dot = 0.0
@@ -83,4 +87,5 @@ def attention_brute(q, k_nope, v, rope, cache_lengths, valid_length, cache_row_o
                     for d in range(128):
                         acc[d] += w * v[g][h][d]
                 out[t][h] = [a / wsum for a in acc]
-    return out
+                lse[t][h] = top + math.log(wsum)
+    return (out, lse) if with_lse else out

@@ -4,9 +4,11 @@ fails.  Nothing here touches the GPU path."""
 import numpy as np
 import pytest
 
+import oracle
 import oracle.mla_oracle as om
 from tests import test_oracle_attention as A
 from tests import test_oracle_fp8 as F
+from tests import test_oracle_masks_merge as M
 
 
 def _pins():
@@ -17,6 +19,13 @@ def _pins():
              A.test_concatenated_rope_equals_standard_attention, A.test_prefix_consistency,
              A.test_page_permutation_invariance, A.test_head_and_batch_independence,
              A.test_query_with_no_visible_key_is_zero, F.test_fp8_attention_is_attention_of_dequantised_values]
+    pins += [lambda c=c: M.test_null_mask_matches_brute_force(c) for c in range(len(M.NULL_CASES))]
+    pins += [lambda c=c: M.test_lse_matches_brute_force(c) for c in range(len(M.LSE_CASES))]
+    pins += [M.test_null_mask_zero_query_gives_mean_of_all_values, M.test_null_mask_last_token_equals_causal,
+             M.test_lse_single_key_is_the_scaled_score, M.test_lse_of_zero_query_is_log_of_key_count,
+             M.test_lse_shift_by_constant_score, M.test_merge_two_single_key_partials_closed_form,
+             M.test_merge_with_empty_side_is_identity, M.test_merge_is_symmetric_and_associative]
+    pins += [lambda c=c: M.test_rows_merged_equal_single_row(c) for c in range(len(M.MULTI_ROW_CASES))]
     return pins
 
 
@@ -31,26 +40,72 @@ def _count_failures():
 
 
 _orig_attend = om._attend
+_orig_visible = om._visible
 _orig_rope = om.rope_rows
+_orig_merge = om.merge_partials
 
 
-def _attend_no_rope(q, kn, kr, v, scale, qpos, kpos):
-    return _orig_attend(np.concatenate([q[:, :128], np.zeros_like(q[:, 128:])], axis=1), kn, kr, v, scale, qpos, kpos)
+def _attend_no_rope(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
+    return _orig_attend(np.concatenate([q[:, :128], np.zeros_like(q[:, 128:])], axis=1), kn, kr, v, scale, qpos, kpos, mask)
 
 
-def _attend_scale_nope_only(q, kn, kr, v, scale, qpos, kpos):
+def _attend_scale_nope_only(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
     q2 = q.copy()
     if scale != 0:
         q2[:, 128:] /= scale
-    return _orig_attend(q2, kn, kr, v, scale, qpos, kpos)
+    return _orig_attend(q2, kn, kr, v, scale, qpos, kpos, mask)
 
 
-def _attend_values_are_keys(q, kn, kr, v, scale, qpos, kpos):
-    return _orig_attend(q, kn, kr, kn, scale, qpos, kpos)
+def _attend_values_are_keys(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
+    return _orig_attend(q, kn, kr, kn, scale, qpos, kpos, mask)
 
 
-def _attend_rope_negated(q, kn, kr, v, scale, qpos, kpos):
-    return _orig_attend(q, kn, -kr, v, scale, qpos, kpos)
+def _attend_rope_negated(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
+    return _orig_attend(q, kn, -kr, v, scale, qpos, kpos, mask)
+
+
+def _attend_lse_no_max(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
+    """lse = ln(sum exp(score - max)), the max shift left out."""
+    o, lse = _orig_attend(q, kn, kr, v, scale, qpos, kpos, mask)
+    if len(q) == 0 or len(kpos) == 0:
+        return o, lse
+    s = scale * (q[:, :128] @ kn.T + q[:, 128:] @ kr.T)
+    s = np.where(_orig_visible(qpos, kpos, mask), s, -np.inf)
+    top = s.max(axis=1)
+    return o, np.where(np.isfinite(lse), lse - np.where(np.isfinite(top), top, 0.0), lse)
+
+
+def _attend_lse_log2(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
+    o, lse = _orig_attend(q, kn, kr, v, scale, qpos, kpos, mask)
+    return o, lse / np.log(2.0)
+
+
+def _attend_lse_unscaled(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
+    o, _ = _orig_attend(q, kn, kr, v, scale, qpos, kpos, mask)
+    _, lse = _orig_attend(q, kn, kr, v, 1.0, qpos, kpos, mask)
+    return o, lse
+
+
+def _merge_plain_average(o_a, lse_a, o_b, lse_b):
+    o, lse = _orig_merge(o_a, lse_a, o_b, lse_b)
+    fa, fb = np.isfinite(lse_a), np.isfinite(lse_b)
+    avg = np.where((fa & fb)[..., None], 0.5 * (o_a + o_b), np.where(fa[..., None], o_a, o_b))
+    return np.where(np.isfinite(lse)[..., None], avg, 0.0), lse
+
+
+def _merge_max_only(o_a, lse_a, o_b, lse_b):
+    o, lse = _orig_merge(o_a, lse_a, o_b, lse_b)
+    pick = np.where((np.asarray(lse_a) >= np.asarray(lse_b))[..., None], o_a, o_b)
+    return np.where(np.isfinite(lse)[..., None], pick, 0.0), np.maximum(lse_a, lse_b)
+
+
+def _merge_swapped(o_a, lse_a, o_b, lse_b):
+    o, lse = _orig_merge(o_a, lse_a, o_b, lse_b)
+    some = np.isfinite(lse)
+    safe = np.where(some, lse, 0.0)
+    wa = np.where(some, np.exp(np.asarray(lse_b) - safe), 0.0)
+    wb = np.where(some, np.exp(np.asarray(lse_a) - safe), 0.0)
+    return wa[..., None] * o_a + wb[..., None] * o_b, lse
 
 
 def _rope_logical_pages(cache, layer_idx, page_table, page_size, rope_col, b, positions):
@@ -73,7 +128,19 @@ MUTATIONS = {
     "scale on the nope term only": ("_attend", _attend_scale_nope_only),
     "keys used as values": ("_attend", _attend_values_are_keys),
     "rope sign flipped": ("_attend", _attend_rope_negated),
-    "exclusive diagonal": ("_visible", lambda qpos, kpos: kpos[None, :] < qpos[:, None]),
+    "exclusive diagonal": ("_visible", lambda qpos, kpos, mask="causal":
+                           kpos[None, :] < qpos[:, None] if mask == "causal" else _orig_visible(qpos, kpos, mask)),
+    "null mask applies the causal predicate": ("_visible", lambda qpos, kpos, mask="causal":
+                                               _orig_visible(qpos, kpos, "causal")),
+    "null mask hides the diagonal": ("_visible", lambda qpos, kpos, mask="causal":
+                                     _orig_visible(qpos, kpos, mask) & (kpos[None, :] != qpos[:, None])
+                                     if mask == "null" else _orig_visible(qpos, kpos, mask)),
+    "lse without the max shift": ("_attend", _attend_lse_no_max),
+    "lse in log2 units": ("_attend", _attend_lse_log2),
+    "lse of unscaled scores": ("_attend", _attend_lse_unscaled),
+    "merge by plain average": ("merge_partials", _merge_plain_average),
+    "merge by the larger lse only": ("merge_partials", _merge_max_only),
+    "merge weights swapped": ("merge_partials", _merge_swapped),
     "mask ignores the prefix": ("_query_positions", lambda p, b, count: np.arange(count, dtype=np.int64)),
     "cache_offsets ignored": ("_key_positions", lambda co, b, count: np.arange(count, dtype=np.int64)),
     "page table ignored": ("rope_rows", _rope_logical_pages),
@@ -95,4 +162,6 @@ def test_unmutated_oracle_passes_every_pin():
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(om, attr, fn)
+    if hasattr(oracle, attr):            # names the pins call through the package
+        monkeypatch.setattr(oracle, attr, fn)
     assert _count_failures() >= 1, f"no pin caught: {name}"
