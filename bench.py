@@ -152,6 +152,72 @@ def gather_bench(torch, batch=64, n_range=(8192, 24576), width=576, page_size=12
             "pct_of_hbm_peak": round(100 * moved / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 1), "sample_rows_exact": exact}
 
 
+def _median_ms(torch, fn, reps, stream):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return ms[len(ms) // 2], ms[0]
+
+
+def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
+    """The paths beside the headline step, on the same workload:
+    the null mask (every key visible), the context cut into three buffer rows
+    whose partials merge in the attention epilogue, and the standalone merge
+    kernel's bandwidth on fp32 partials."""
+    from mla_ragged_paged_amd import _binding as B
+    from mla_ragged_paged_amd import workloads
+    from mla_ragged_paged_amd.pipeline import PrefillStep
+    stream = torch.cuda.current_stream()
+    peak = PEAK_TFLOPS[w.spec.dtype]
+    out = {}
+
+    nm = PrefillStep(w, "cuda:0", mask="null")
+    nm.run()
+    med, best = _median_ms(torch, lambda: nm.attention(0), reps, stream)
+    fl = workloads.null_mask_flops(w.n, w.p, w.heads)
+    out["null_mask"] = {"attention_median_ms": round(med, 4), "attention_min_ms": round(best, 4),
+                        "tflop": round(fl / 1e12, 5), "achieved_TFLOPs": round(fl / (med * 1e-3) / 1e12, 2),
+                        "frac_of_peak": round(fl / (med * 1e-3) / 1e12 / peak, 4)}
+    del nm
+
+    cap = -(-w.total_ctx // 3)
+    mr = PrefillStep(w, "cuda:0", cap=cap)
+    mr.run()
+    step_med, _ = _median_ms(torch, mr.run, reps, stream)
+
+    def rows_attention():
+        for r in range(mr.rows):
+            mr.attention_row_merged(r)
+    attn_med, attn_best = _median_ms(torch, rows_attention, reps, stream)
+    fl = workloads.causal_flops(w.n, w.p, w.heads)
+    out["rows_merged"] = {"cap": cap, "rows": mr.rows, "step_median_ms": round(step_med, 4),
+                          "attention_median_ms": round(attn_med, 4), "attention_min_ms": round(attn_best, 4),
+                          "achieved_TFLOPs": round(fl / (attn_med * 1e-3) / 1e12, 2),
+                          "frac_of_peak": round(fl / (attn_med * 1e-3) / 1e12 / peak, 4),
+                          "attention_time_vs_one_row": round(attn_med / one_row_attention_ms, 3)}
+    del mr
+
+    T, H = 16384, 128
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(12)
+    o_a = torch.randn((T, H, 128), generator=gen, device=dev)
+    o_b = torch.randn((T, H, 128), generator=gen, device=dev)
+    l_a = torch.randn((T, H), generator=gen, device=dev)
+    l_b = torch.randn((T, H), generator=gen, device=dev)
+    o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    B.mla_prefill_merge(o, None, o_a, l_a, o_b, l_b)
+    med, best = _median_ms(torch, lambda: B.mla_prefill_merge(o, None, o_a, l_a, o_b, l_b), reps, stream)
+    moved = T * H * (2 * 128 * 4 + 2 * 4 + 128 * 2)
+    out["merge_kernel"] = {"tokens": T, "heads": H, "output": "bf16", "bytes_moved": moved,
+                           "median_ms": round(med, 4), "GBps": round(moved / (med * 1e-3) / 1e9, 1),
+                           "pct_of_hbm_peak": round(100 * moved / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -160,7 +226,7 @@ def main():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-extras", action="store_true", help="skip the cold-cache and gather-bandwidth measurements")
+    ap.add_argument("--no-extras", action="store_true", help="skip the cold-cache, gather-bandwidth, null-mask, buffer-row and merge measurements")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (scales HBM byte counters)")
     args = ap.parse_args()
@@ -272,6 +338,8 @@ def main():
                                 "achieved_TFLOPs_median": round(flops / (cold[len(cold) // 2] * 1e-3) / 1e12, 2)}
         print("[bench] gather bandwidth on a >= 1 GiB paged cache", file=sys.stderr, flush=True)
         result["gather_bench"] = gather_bench(torch)
+        print("[bench] null mask, three buffer rows merged, merge kernel", file=sys.stderr, flush=True)
+        result["next_rows"] = next_rows_bench(torch, w, attn_median)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

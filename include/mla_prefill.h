@@ -8,10 +8,19 @@
  *   mla_prefill_gather  copies one buffer row's cache entries out of the paged
  *                       cache into a contiguous buffer (same page, description: the
  *                       plan exists so that K/V entries can be gathered);
- *   mla_prefill_ragged  causal attention of ragged Q [T,H,192] over the ragged
- *                       K_nope/V buffer [rows,H,128] and the shared, paged
- *                       K_rope [positions,1,64] (page "flare_mla_prefill";
- *                       launch shape and argument meanings of page "mla_prefill_v2_ragged").
+ *   mla_prefill_ragged  masked (causal or null) attention of ragged Q [T,H,192]
+ *                       over the ragged K_nope/V buffer [rows,H,128] and the
+ *                       shared, paged K_rope [positions,1,64] (page
+ *                       "flare_mla_prefill"; launch shape and argument meanings
+ *                       of page "mla_prefill_v2_ragged").
+ *
+ * When the plan cuts the contexts over several buffer rows, each row's
+ * attention covers part of a sequence's keys:
+ *
+ *   mla_prefill_ragged_lse  the same attention, also writing each (token, head)'s
+ *                           log-sum-exp, optionally merged in place with the
+ *                           partial result of earlier rows;
+ *   mla_prefill_merge       log-sum-exp combine of two partial results.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked [host].  Device arrays are
@@ -21,7 +30,7 @@
  *     synchronises.  The caller owns all memory and keeps it alive and unchanged
  *     until the enqueued work has finished.  The library allocates no device
  *     memory and keeps no state beyond its loaded code objects; calls are
- *     thread-safe.  Outputs must not alias inputs.
+ *     thread-safe.  Outputs must not alias inputs, except where a call says so.
  *   - Host-checkable errors are returned before anything is enqueued (nothing
  *     is written).  Properties of device data (monotone offsets, in-range page
  *     ids, lengths) are preconditions that are NOT checked: violating them is
@@ -50,13 +59,17 @@ typedef enum {
 } mla_status_t;
 
 /* Element types ("flare_mla_prefill", Parameters: q is bfloat16 or float8_e4m3fn;
- * the output is bfloat16 when q is float8_e4m3fn, else the type of q). */
-typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3FN = 1 } mla_dtype_t;
+ * the output is bfloat16 when q is float8_e4m3fn, else the type of q).
+ * MLA_FP32 is offered for outputs only: partial results that are merged later
+ * keep full precision. */
+typedef enum { MLA_BF16 = 0, MLA_FP8_E4M3FN = 1, MLA_FP32 = 2 } mla_dtype_t;
 
-/* Mask predicates ("mla_prefill_v2_ragged", Args: mask_functor). Only the causal
- * mask is offered: key position kpos is visible to query position qpos iff
- * kpos <= qpos. */
-typedef enum { MLA_MASK_CAUSAL = 0 } mla_mask_t;
+/* Mask predicates ("mla_prefill_v2_ragged", Parameters and Args: mask_t and
+ * mask_functor, "causal, null, etc."):
+ *   MLA_MASK_CAUSAL  key position kpos is visible to query position qpos iff kpos <= qpos;
+ *   MLA_MASK_NULL    no predicate: every key the call is given for sequence b is
+ *                    visible to every new token of b. */
+typedef enum { MLA_MASK_CAUSAL = 0, MLA_MASK_NULL = 1 } mla_mask_t;
 
 /* Largest batch the plan and gather kernels accept (their per-sequence offsets
  * are staged in on-chip memory). */
@@ -166,7 +179,8 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
  *   output[t][h][:] = sum_{j visible} softmax_j(s) * v[g][h][:]
  * where K_rope(b, pos) is the 64-wide column window at kv->rope_col of the cache
  * row of sequence b at position pos in layer layer_idx (one row shared by all
- * heads), "visible" means kpos <= qpos, and a query with no visible key gets 0.
+ * heads), "visible" means kpos <= qpos under MLA_MASK_CAUSAL and every j under
+ * MLA_MASK_NULL, and a query with no visible key gets 0.
  *
  *   output            device [total_q_tokens][num_heads][128], output_dtype.
  *   q                 device [total_q_tokens][num_heads][192], qkv_dtype
@@ -185,8 +199,9 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
  *                     (K_rope uses kv->scale); must be NULL for bf16.
  *   q_max_seq_len     upper bound on n_b (bounds the launch); 0 = total_q_tokens.
  *                     A value below some n_b is a precondition violation.
- * Dtypes: (qkv, output) = (MLA_BF16, MLA_BF16) or (MLA_FP8_E4M3FN, MLA_BF16).
- * Accumulation is fp32; the output is rounded to bf16 (nearest-even).
+ *   mask              MLA_MASK_CAUSAL or MLA_MASK_NULL.
+ * Dtypes: qkv MLA_BF16 or MLA_FP8_E4M3FN; output MLA_BF16 (the pages' type) or
+ * MLA_FP32.  Accumulation is fp32; a bf16 output is rounded to nearest-even.
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED_DTYPE, UNSUPPORTED_DIMS,
  * UNSUPPORTED_MASK, HIP.
  */
@@ -198,6 +213,72 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
                                 uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
                                 const float* q_scale, const float* k_nope_scale, const float* v_scale,
                                 uint32_t q_max_seq_len, void* stream);
+
+/*
+ * mla_prefill_ragged_lse -- the attention of mla_prefill_ragged for one buffer
+ * row of the plan (page "generic_flare_mla_prefill_ragged_paged_plan",
+ * description and Args: a row holds part of each sequence's cached context),
+ * with the log-sum-exp a later merge needs.
+ *
+ * All arguments from q on are those of mla_prefill_ragged, with the same
+ * meaning and checks.  For every token t and head h the call computes the
+ * softmax result o over the keys it is given, as mla_prefill_ragged does, and
+ *   lse_self[t][h] = ln( sum_{j visible} exp(s_j) )        (-inf: no visible key)
+ * with s_j the scaled scores above.  Then:
+ *   prev_output == NULL:  output = o, lse = lse_self;
+ *   otherwise (a partial over other keys of the same tokens), the softmax over
+ *   the union:  L = ln(exp(prev_lse) + exp(lse_self)),
+ *               output = exp(prev_lse - L) * prev_output + exp(lse_self - L) * o,
+ *               lse = L   (both -inf: output 0, lse -inf).
+ * Running the call once per buffer row, passing the previous call's fp32
+ * output and lse as prev_*, therefore yields the attention over every key.
+ *
+ *   output        device [total_q_tokens][num_heads][128], MLA_BF16 or MLA_FP32.
+ *   lse           device fp32 [total_q_tokens][num_heads] or NULL (not written).
+ *   prev_output   device fp32 [total_q_tokens][num_heads][128] or NULL; may be
+ *                 the same buffer as `output` when output_dtype is MLA_FP32.
+ *   prev_lse      device fp32 [total_q_tokens][num_heads]; NULL exactly when
+ *                 prev_output is; may be the same buffer as `lse`.
+ * Every (t, h) with t < total_q_tokens inside some sequence is written on every
+ * call, also where this call sees no key (it then passes prev_* through).
+ * prev_output is not read where its weight is 0 (prev_lse = -inf).
+ * Errors: those of mla_prefill_ragged; NULL_ARG when exactly one of prev_output
+ * and prev_lse is NULL; BAD_SHAPE for fp32 arrays not 4-byte (lse) or 16-byte
+ * (prev_output) aligned.
+ */
+mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, float* lse,
+                                    const float* prev_output, const float* prev_lse,
+                                    const void* q, mla_dtype_t qkv_dtype, const void* k_nope, const void* v,
+                                    const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                    const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                    const uint32_t* cache_offsets, uint32_t batch_size,
+                                    uint32_t total_q_tokens, uint32_t num_heads, uint32_t q_depth,
+                                    uint32_t depth, mla_mask_t mask, float scale, const float* q_scale,
+                                    const float* k_nope_scale, const float* v_scale,
+                                    uint32_t q_max_seq_len, void* stream);
+
+/*
+ * mla_prefill_merge -- combine two partial attention results over disjoint key
+ * sets of the same tokens (buffer rows of page
+ * "generic_flare_mla_prefill_ragged_paged_plan"; see mla_prefill_ragged_lse).
+ * For every row r < total_q_tokens * num_heads:
+ *   L = ln(exp(lse_a[r]) + exp(lse_b[r])),
+ *   output[r][:] = exp(lse_a[r] - L) * o_a[r][:] + exp(lse_b[r] - L) * o_b[r][:],
+ *   lse[r] = L          (lse_a = lse_b = -inf: output 0, lse -inf).
+ * A side whose weight is 0 is not read.
+ *
+ *   output      device [total_q_tokens][num_heads][depth], MLA_BF16 or MLA_FP32;
+ *               may be o_a or o_b when MLA_FP32.
+ *   lse         device fp32 [total_q_tokens][num_heads] or NULL; may be lse_a or lse_b.
+ *   o_a, o_b    device fp32 [total_q_tokens][num_heads][depth].
+ *   lse_a, lse_b device fp32 [total_q_tokens][num_heads] (natural log).
+ *   depth       must be 128.
+ * Errors: NULL_ARG, UNSUPPORTED_DIMS, UNSUPPORTED_DTYPE, BAD_SHAPE (alignment:
+ * 16 bytes for output, o_a, o_b; 4 for the lse arrays), HIP.
+ */
+mla_status_t mla_prefill_merge(void* output, mla_dtype_t output_dtype, float* lse, const float* o_a,
+                               const float* lse_a, const float* o_b, const float* lse_b,
+                               uint32_t total_q_tokens, uint32_t num_heads, uint32_t depth, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* mla_status_string(mla_status_t status);

@@ -9,7 +9,9 @@ been built; there is no fallback.
 from ._binding import (  # noqa: F401
     MLA_BF16,
     MLA_FP8_E4M3FN,
+    MLA_FP32,
     MLA_MASK_CAUSAL,
+    MLA_MASK_NULL,
     MLA_MAX_BATCH,
     MlaError,
     PagedCache,
@@ -17,6 +19,8 @@ from ._binding import (  # noqa: F401
     mla_prefill_gather,
     mla_prefill_last_hip_error,
     mla_prefill_plan,
+    mla_prefill_merge,
     mla_prefill_ragged,
+    mla_prefill_ragged_lse,
     mla_status_string,
 )

@@ -19,7 +19,10 @@ _LIB_PATH = os.path.join(_PKG, "libmla_prefill.so")
 
 MLA_BF16 = 0
 MLA_FP8_E4M3FN = 1
+MLA_FP32 = 2
 MLA_MASK_CAUSAL = 0
+MLA_MASK_NULL = 1
+_MASKS = {"causal": MLA_MASK_CAUSAL, "null": MLA_MASK_NULL}
 MLA_MAX_BATCH = 8192
 
 _STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_SHAPE", 3: "MLA_ERR_UNSUPPORTED_DTYPE",
@@ -61,6 +64,11 @@ def _load():
     lib.mla_prefill_ragged.argtypes = [vp, i32, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32, u32, u32, u32,
                                        i32, ctypes.c_float, vp, vp, vp, u32, vp]
     lib.mla_prefill_ragged.restype = i32
+    lib.mla_prefill_ragged_lse.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32, u32,
+                                           u32, u32, i32, ctypes.c_float, vp, vp, vp, u32, vp]
+    lib.mla_prefill_ragged_lse.restype = i32
+    lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
+    lib.mla_prefill_merge.restype = i32
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_prefill_last_hip_error.argtypes = []
@@ -102,6 +110,8 @@ def _stream(stream):
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return MLA_BF16
+    if t.dtype == torch.float32:
+        return MLA_FP32
     if t.dtype in (torch.float8_e4m3fn, torch.uint8):
         return MLA_FP8_E4M3FN
     raise TypeError(f"unsupported dtype {t.dtype}")
@@ -161,19 +171,80 @@ def mla_prefill_gather(kv: PagedCache, layer_idx, buffer_row_offsets_r, cache_of
                                    _ptr(out), _stream(stream)), "mla_prefill_gather")
 
 
+def _mask_code(mask) -> int:
+    if mask not in _MASKS:
+        raise ValueError(f"mask must be one of {sorted(_MASKS)}, got {mask!r}")
+    return _MASKS[mask]
+
+
+def _contiguous(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _shapes(T, H, rows=(), lses=()):
+    """Output-side arrays must be [T, H, 128] (rows) and [T, H] (lses): the kernels
+    touch every (token, head)."""
+    for name, t in rows:
+        if t is not None and tuple(t.shape) != (T, H, 128):
+            raise ValueError(f"{name} must have shape {(T, H, 128)}, got {tuple(t.shape)}")
+    for name, t in lses:
+        if t is not None and tuple(t.shape) != (T, H):
+            raise ValueError(f"{name} must have shape {(T, H)}, got {tuple(t.shape)}")
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _ptr(t)
+
+
 def mla_prefill_ragged(output, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length, cache_row_offsets,
                        cache_offsets, scale, q_scale=None, k_nope_scale=None, v_scale=None, q_max_seq_len=0,
-                       stream=None):
-    """Causal MLA prefill: output [T, H, 128] from q [T, H, 192] and the ragged K/V buffer."""
+                       stream=None, mask="causal"):
+    """MLA prefill: output [T, H, 128] (bf16 or fp32) from q [T, H, 192] and the ragged K/V buffer.
+
+    ``mask`` is "causal" or "null"."""
     T, H, qd = q.shape
-    for t, name in ((output, "output"), (q, "q"), (k_nope, "k_nope"), (v, "v")):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _contiguous(output=output, q=q, k_nope=k_nope, v=v)
+    _shapes(T, H, rows=[("output", output)])
     s = k_rope.as_struct()
     _check(_lib.mla_prefill_ragged(_ptr(output), _dtype_code(output), _ptr(q), _dtype_code(q), _ptr(k_nope),
                                    _ptr(v), ctypes.byref(s), layer_idx, _idx(valid_length, "valid_length"),
                                    _idx(cache_row_offsets, "cache_row_offsets"),
                                    _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H, qd,
-                                   k_nope.shape[2], MLA_MASK_CAUSAL, float(scale), _ptr(q_scale),
+                                   k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
                                    _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
            "mla_prefill_ragged")
+
+
+def mla_prefill_ragged_lse(output, lse, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length,
+                           cache_row_offsets, cache_offsets, scale, prev_output=None, prev_lse=None, q_scale=None,
+                           k_nope_scale=None, v_scale=None, q_max_seq_len=0, stream=None, mask="causal"):
+    """One buffer row's attention with its log-sum-exp lse [T, H] (float32, or None),
+    merged with an earlier partial (prev_output fp32 [T, H, 128], prev_lse [T, H]) when given.
+    output / lse may be the same tensors as prev_output / prev_lse."""
+    T, H, qd = q.shape
+    _contiguous(output=output, lse=lse, q=q, k_nope=k_nope, v=v, prev_output=prev_output, prev_lse=prev_lse)
+    _shapes(T, H, rows=[("output", output), ("prev_output", prev_output)], lses=[("lse", lse), ("prev_lse", prev_lse)])
+    s = k_rope.as_struct()
+    _check(_lib.mla_prefill_ragged_lse(_ptr(output), _dtype_code(output), _f32(lse, "lse"),
+                                       _f32(prev_output, "prev_output"), _f32(prev_lse, "prev_lse"), _ptr(q),
+                                       _dtype_code(q), _ptr(k_nope), _ptr(v), ctypes.byref(s), layer_idx,
+                                       _idx(valid_length, "valid_length"),
+                                       _idx(cache_row_offsets, "cache_row_offsets"),
+                                       _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H, qd,
+                                       k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
+                                       _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
+           "mla_prefill_ragged_lse")
+
+
+def mla_prefill_merge(output, lse, o_a, lse_a, o_b, lse_b, stream=None):
+    """Log-sum-exp combine of two partials: output [T, H, 128] (bf16 or fp32), lse [T, H] or None."""
+    T, H, D = o_a.shape
+    _contiguous(output=output, lse=lse, o_a=o_a, lse_a=lse_a, o_b=o_b, lse_b=lse_b)
+    _shapes(T, H, rows=[("output", output), ("o_b", o_b)], lses=[("lse", lse), ("lse_a", lse_a), ("lse_b", lse_b)])
+    _check(_lib.mla_prefill_merge(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _f32(o_a, "o_a"),
+                                  _f32(lse_a, "lse_a"), _f32(o_b, "o_b"), _f32(lse_b, "lse_b"), T, H, D,
+                                  _stream(stream)), "mla_prefill_merge")

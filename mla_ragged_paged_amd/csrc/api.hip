@@ -16,7 +16,7 @@ mla_status_t hip_status(hipError_t e) {
   return MLA_ERR_HIP;
 }
 
-size_t dtype_bytes(mla_dtype_t t) { return t == MLA_FP8_E4M3FN ? 1 : 2; }
+size_t dtype_bytes(mla_dtype_t t) { return t == MLA_FP8_E4M3FN ? 1 : t == MLA_FP32 ? 4 : 2; }
 
 bool dtype_known(mla_dtype_t t) { return t == MLA_BF16 || t == MLA_FP8_E4M3FN; }
 
@@ -46,7 +46,7 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE: inconsistent or unsupported sizes";
     case MLA_ERR_UNSUPPORTED_DTYPE: return "MLA_ERR_UNSUPPORTED_DTYPE: dtype combination not offered";
     case MLA_ERR_UNSUPPORTED_DIMS: return "MLA_ERR_UNSUPPORTED_DIMS: q_depth must be 192 and depth 128";
-    case MLA_ERR_UNSUPPORTED_MASK: return "MLA_ERR_UNSUPPORTED_MASK: only the causal mask is offered";
+    case MLA_ERR_UNSUPPORTED_MASK: return "MLA_ERR_UNSUPPORTED_MASK: the mask is neither causal nor null";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported an error";
   }
   return "unknown mla_status_t";
@@ -109,19 +109,22 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
   return hip_status(mla::launch_gather(a, unit, static_cast<hipStream_t>(stream)));
 }
 
-mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
-                                const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
-                                uint32_t layer_idx, const uint32_t* valid_length, const uint32_t* cache_row_offsets,
-                                const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
-                                uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
-                                const float* q_scale, const float* k_nope_scale, const float* v_scale,
-                                uint32_t q_max_seq_len, void* stream) {
+mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, float* lse, const float* prev_output,
+                                    const float* prev_lse, const void* q, mla_dtype_t qkv_dtype, const void* k_nope,
+                                    const void* v, const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                    const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                    const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                    uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
+                                    float scale, const float* q_scale, const float* k_nope_scale,
+                                    const float* v_scale, uint32_t q_max_seq_len, void* stream) {
   if (!output || !q || !k_nope || !v || !valid_length || !cache_row_offsets) return MLA_ERR_NULL_ARG;
+  if ((prev_output == nullptr) != (prev_lse == nullptr)) return MLA_ERR_NULL_ARG;
   mla_status_t st = check_cache(k_rope, layer_idx);
   if (st != MLA_OK) return st;
   if (q_depth != 192 || depth != 128) return MLA_ERR_UNSUPPORTED_DIMS;
-  if (mask != MLA_MASK_CAUSAL) return MLA_ERR_UNSUPPORTED_MASK;
-  if (!dtype_known(qkv_dtype) || output_dtype != MLA_BF16 || k_rope->dtype != qkv_dtype)
+  if (mask != MLA_MASK_CAUSAL && mask != MLA_MASK_NULL) return MLA_ERR_UNSUPPORTED_MASK;
+  if (!dtype_known(qkv_dtype) || (output_dtype != MLA_BF16 && output_dtype != MLA_FP32) ||
+      k_rope->dtype != qkv_dtype)
     return MLA_ERR_UNSUPPORTED_DTYPE;
   const bool fp8 = qkv_dtype == MLA_FP8_E4M3FN;
   if (fp8 && (!q_scale || !k_nope_scale || !v_scale || !k_rope->scale)) return MLA_ERR_NULL_ARG;
@@ -133,7 +136,9 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
   if ((k_rope->rope_col * el) % 16 || (k_rope->row_width * el) % 16 || (uint64_t)k_rope->rope_col + 64 > k_rope->row_width)
     return MLA_ERR_BAD_SHAPE;
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_nope) | reinterpret_cast<uintptr_t>(v) |
-       reinterpret_cast<uintptr_t>(k_rope->data) | reinterpret_cast<uintptr_t>(output)) % 16)
+       reinterpret_cast<uintptr_t>(k_rope->data) | reinterpret_cast<uintptr_t>(output) |
+       reinterpret_cast<uintptr_t>(prev_output)) % 16 ||
+      (reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(prev_lse)) % 4)
     return MLA_ERR_BAD_SHAPE;
   // the kernels address one sequence's rows and one cache layer with 32-bit byte offsets
   const uint64_t layer_bytes = (uint64_t)k_rope->num_pages * k_rope->page_size * k_rope->row_width * el;
@@ -145,6 +150,11 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
 
   mla::PrefillArgs a{};
   a.out = output;
+  a.lse = lse;
+  a.prev_out = prev_output;
+  a.prev_lse = prev_lse;
+  a.out_fp32 = output_dtype == MLA_FP32 ? 1u : 0u;
+  a.causal = mask == MLA_MASK_CAUSAL ? 1u : 0u;
   a.q = q;
   a.k_nope = k_nope;
   a.v = v;
@@ -175,6 +185,43 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp8) return hip_status(mla::launch_prefill_fp8(a, q_max, s));
   return hip_status(mla::launch_prefill_bf16(a, q_max, s));
+}
+
+mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
+                                const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
+                                uint32_t layer_idx, const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
+                                const float* q_scale, const float* k_nope_scale, const float* v_scale,
+                                uint32_t q_max_seq_len, void* stream) {
+  return mla_prefill_ragged_lse(output, output_dtype, nullptr, nullptr, nullptr, q, qkv_dtype, k_nope, v, k_rope,
+                                layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
+                                total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale,
+                                v_scale, q_max_seq_len, stream);
+}
+
+mla_status_t mla_prefill_merge(void* output, mla_dtype_t output_dtype, float* lse, const float* o_a,
+                               const float* lse_a, const float* o_b, const float* lse_b, uint32_t total_q_tokens,
+                               uint32_t num_heads, uint32_t depth, void* stream) {
+  if (!output || !o_a || !lse_a || !o_b || !lse_b) return MLA_ERR_NULL_ARG;
+  if (depth != 128) return MLA_ERR_UNSUPPORTED_DIMS;
+  if (output_dtype != MLA_BF16 && output_dtype != MLA_FP32) return MLA_ERR_UNSUPPORTED_DTYPE;
+  if (total_q_tokens == 0 || num_heads == 0) return MLA_OK;
+  if ((reinterpret_cast<uintptr_t>(output) | reinterpret_cast<uintptr_t>(o_a) | reinterpret_cast<uintptr_t>(o_b)) % 16 ||
+      (reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(lse_a) | reinterpret_cast<uintptr_t>(lse_b)) % 4)
+    return MLA_ERR_BAD_SHAPE;
+  const uint64_t rows = (uint64_t)total_q_tokens * num_heads;
+  if (rows * 32 / 256 >= (1ull << 31)) return MLA_ERR_BAD_SHAPE;
+  mla::MergeArgs a{};
+  a.out = output;
+  a.lse = lse;
+  a.o_a = o_a;
+  a.lse_a = lse_a;
+  a.o_b = o_b;
+  a.lse_b = lse_b;
+  a.rows = rows;
+  a.out_fp32 = output_dtype == MLA_FP32 ? 1u : 0u;
+  return hip_status(mla::launch_merge(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

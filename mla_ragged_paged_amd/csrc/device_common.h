@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace mla {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -38,6 +40,86 @@ __device__ __forceinline__ float swap_halves(float x) {
 __device__ __forceinline__ float max_across_halves(float x) {
   u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+constexpr float LOG2E_F = 1.4426950408889634f;
+constexpr float LN2_F = 0.6931471805599453f;
+
+// Combine weights of two partial softmax results from their log-sum-exps
+// (natural log): the union's lse is ln(e^la + e^lb) and each side weighs
+// e^(l_x - lse).  Both sides empty (-inf) gives weights 0 and lse -inf; one side
+// empty passes the other through exactly (weight 1, its lse unchanged).
+struct MergeWeights {
+  float wa, wb, lse;
+};
+__device__ __forceinline__ MergeWeights merge_weights(float la, float lb) {
+  const float mm = fmaxf(la, lb);
+  if (mm == -INFINITY) return MergeWeights{0.f, 0.f, -INFINITY};
+  const float ea = __builtin_amdgcn_exp2f((la - mm) * LOG2E_F);
+  const float eb = __builtin_amdgcn_exp2f((lb - mm) * LOG2E_F);
+  const float sum = ea + eb;                       // in [1, 2]
+  return MergeWeights{ea / sum, eb / sum, mm + __builtin_amdgcn_logf(sum) * LN2_F};
+}
+
+// Stores one lane's share of a finished query row (row = token * H + head).
+// o[d][4g + k] is output column 32d + 8g + 4hf + k before normalisation, `inv`
+// normalises it, and lse2 is the row's log-sum-exp in log2 units (-inf when the
+// call saw no key for the row).  With an earlier partial in a.prev_out /
+// a.prev_lse the two are combined by merge_weights; the earlier side is read
+// only where its weight is non-zero.  The output is written as bf16 (rounded
+// to nearest-even) or fp32, and the lower half's lanes store the
+// log-sum-exp, in natural-log units, when a.lse is set.  Each lane reads the
+// earlier partial's elements before it writes them, so out / lse may be the
+// same buffers as prev_out / prev_lse.
+// PLAIN: bf16 output, no log-sum-exp, no earlier partial (the fields are not read).
+template <bool PLAIN>
+__device__ __forceinline__ void store_output_row(const PrefillArgs& a, size_t row, int hf, const f32x16 (&o)[4],
+                                                 float inv, float lse2) {
+  if constexpr (PLAIN) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dv = d * 32 + g * 8 + hf * 4;
+        const uint32_t w0 = pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * 128 + dv) = u32x2{w0, w1};
+      }
+    }
+    return;
+  }
+  float w_self = inv, w_prev = 0.f;
+  float lse = lse2 * LN2_F;
+  const float* prev = nullptr;
+  if (a.prev_out) {
+    const MergeWeights mw = merge_weights(a.prev_lse[row], lse);
+    w_self = inv * mw.wb;
+    w_prev = mw.wa;
+    lse = mw.lse;
+    if (w_prev > 0.f) prev = a.prev_out + row * 128;
+  }
+  if (a.lse && hf == 0) a.lse[row] = lse;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dv = d * 32 + g * 8 + hf * 4;
+      f32x4 val = {o[d][4 * g] * w_self, o[d][4 * g + 1] * w_self, o[d][4 * g + 2] * w_self,
+                   o[d][4 * g + 3] * w_self};
+      if (prev) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(prev + dv);
+        val = {__builtin_fmaf(w_prev, pv[0], val[0]), __builtin_fmaf(w_prev, pv[1], val[1]),
+               __builtin_fmaf(w_prev, pv[2], val[2]), __builtin_fmaf(w_prev, pv[3], val[3])};
+      }
+      if (a.out_fp32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * 128 + dv) = val;
+      } else {
+        const uint32_t w0 = pack_bf16x2(val[0], val[1]);
+        const uint32_t w1 = pack_bf16x2(val[2], val[3]);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * 128 + dv) = u32x2{w0, w1};
+      }
+    }
+  }
 }
 
 // One work unit of the prefill kernels: (head, sequence, 128-query tile).

@@ -35,7 +35,10 @@ struct GatherArgs {
 };
 
 struct PrefillArgs {
-  void* out;                          // bf16 [T][H][128]
+  void* out;                          // [T][H][128], bf16 or fp32 (out_fp32)
+  float* lse;                         // [T][H] log-sum-exp (natural log) or nullptr
+  const float* prev_out;              // [T][H][128] fp32 earlier partial or nullptr
+  const float* prev_lse;              // [T][H] its log-sum-exp (with prev_out)
   const void* q;                      // [T][H][192]
   const void* k_nope;                 // [rows][H][128]
   const void* v;                      // [rows][H][128]
@@ -58,13 +61,27 @@ struct PrefillArgs {
   uint32_t batch;
   uint32_t heads;
   uint32_t qtiles;                    // query tiles per sequence (launch bound)
+  uint32_t out_fp32;                  // 1: out is fp32, 0: bf16
+  uint32_t causal;                    // 1: key visible iff kpos <= qpos; 0: every key visible
   float scale;                        // softmax scale (its sign is applied to Q)
   float scale_log2;                   // max(|scale| * log2(e), 1e-30)
+};
+
+struct MergeArgs {
+  void* out;                          // [rows][128], bf16 or fp32 (out_fp32)
+  float* lse;                         // [rows] or nullptr
+  const float* o_a;                   // [rows][128]
+  const float* lse_a;                 // [rows]
+  const float* o_b;
+  const float* lse_b;
+  uint64_t rows;                      // tokens * heads
+  uint32_t out_fp32;
 };
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int unit, hipStream_t stream);
 hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream);
 hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -1,7 +1,9 @@
-// Ragged, causally masked MLA prefill over a paged K_rope cache -- bf16 inputs,
-// bf16 output, fp32 accumulation.  Semantics: page "flare_mla_prefill"
-// (description and Args) with the paged k_rope operand; argument meanings of
-// page "mla_prefill_v2_ragged" (Args).
+// Ragged MLA prefill over a paged K_rope cache -- bf16 inputs, bf16 or fp32
+// output, fp32 accumulation.  Semantics: page "flare_mla_prefill" (description
+// and Args) with the paged k_rope operand; argument meanings of page
+// "mla_prefill_v2_ragged" (Args), whose mask predicate is causal or null here.
+// Each query row's log-sum-exp can be written too, and the row merged with an
+// earlier partial result (another buffer row's keys) in the epilogue.
 //
 // Work unit = (head h, sequence b, query tile of BM = 128 rows).  A workgroup of
 // four waves owns one unit; wave w owns queries [32w, 32w+32) of the tile.
@@ -27,7 +29,8 @@
 //        p is rounded to bf16 once and the row sum is taken over the rounded
 //        values (v_dot2 against (1, 1)), so the weights applied to V are
 //        normalised exactly.  Masks are applied only on tiles that straddle
-//        the causal diagonal or the end of the sequence's keys;
+//        the causal diagonal or the end of the sequence's keys (under the
+//        null mask only the end of the keys);
 //   O^T += V^T . P^T (A = V read transposed out of row-major LDS with
 //        ds_read_b64_tr_b16, B = P^T straight from the S^T registers).  The 16
 //        keys of one MFMA step are taken in the order the S^T accumulator
@@ -73,6 +76,9 @@ __device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 }  // namespace
 
+// CAUSAL: causal mask, else the null mask.  PLAIN: bf16 output only (no
+// log-sum-exp, no earlier partial to merge).
+template <bool CAUSAL, bool PLAIN>
 __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
@@ -92,8 +98,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const int32_t len = (int32_t)(a.cache_row_offsets[b + 1] - g0);
   const int32_t c0 = a.cache_offsets ? (int32_t)a.cache_offsets[b] : 0;
   const int32_t i_last = (int32_t)min(n, i0 + BM) - 1;
-  // keys some query of the tile can see: c0 + j <= p + i_last
-  const int32_t jend = max(0, min(p + i_last - c0 + 1, len));
+  // causal: the keys some query of the tile can see, c0 + j <= p + i_last;
+  // null mask: every key the row holds for the sequence
+  constexpr bool causal = CAUSAL;
+  const int32_t jend = causal ? max(0, min(p + i_last - c0 + 1, len)) : len;
   const int32_t nkt = (jend + BN - 1) / BN;
 
   const int tid = threadIdx.x;
@@ -224,6 +232,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     issue_rope(0, 0, pg0);
   } else {
+    // With no key to attend to, Q is never read (the epilogue writes 0 or passes
+    // an earlier partial through).  The load stays: without this branch the
+    // compiled layout of the kernel changes and the single 16K-token sequence
+    // fell into the start-up regime with ~3x the HBM traffic (measured).
     load_q();
   }
 
@@ -244,7 +256,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       pg_next[1] = page_of(kt + 2, 1);
     }
     const int32_t j0 = kt * BN;
-    if (wave_rows && c0 + j0 <= wq_last) {
+    if (wave_rows && (!causal || c0 + j0 <= wq_last)) {
       const uint8_t* st = lds + stage * STAGE;
       // S^T = K Q^T.  K fragments go through a three-deep register ring, read two
       // k-steps ahead of their MFMAs so LDS latency overlaps the MFMA chain; the
@@ -269,12 +281,12 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       // s[kb][r] is key j0 + 32kb + 4hf + roff(r), roff(r) = 8(r/4) + r%4
-      const bool full = (j0 + BN <= len) && (c0 + j0 + BN - 1 <= wq_first);
+      const bool full = (j0 + BN <= len) && (!causal || c0 + j0 + BN - 1 <= wq_first);
       if (!full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int32_t kbase = j0 + 32 * kb + 4 * hf;
-          const int32_t lim = min(len - 1 - kbase, p + my_i - c0 - kbase);
+          const int32_t lim = causal ? min(len - 1 - kbase, p + my_i - c0 - kbase) : len - 1 - kbase;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int32_t roff = 8 * (r >> 2) + (r & 3);
@@ -342,21 +354,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- epilogue: combine the two halves' row sums, normalise, round to bf16
+  // ---- epilogue: combine the two halves' row sums, normalise, store the row
+  // with its log-sum-exp (merged with an earlier partial when one is given)
   const float l_tot = l_run + swap_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (my_i < (int32_t)n) {
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(t0 + my_i) * H + h) * DV;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dv = d * 32 + g * 8 + hf * 4;
-        const uint32_t w0 = pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + dv) = u32x2{w0, w1};
-      }
-    }
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    store_output_row<PLAIN>(a, (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
   }
 }
 
@@ -365,7 +369,10 @@ hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream
   const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles;
   const uint64_t grid = (units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_bf16_kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
+  const bool plain = !a.out_fp32 && !a.lse && !a.prev_out;
+  auto kernel = a.causal ? (plain ? prefill_bf16_kernel<true, true> : prefill_bf16_kernel<true, false>)
+                         : (plain ? prefill_bf16_kernel<false, true> : prefill_bf16_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

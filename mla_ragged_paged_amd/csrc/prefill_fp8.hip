@@ -1,5 +1,6 @@
-// Ragged, causally masked MLA prefill over a paged K_rope cache -- float8_e4m3fn
-// inputs with per-tensor fp32 scales, bf16 output, fp32 accumulation.
+// Ragged MLA prefill (causal or null mask) over a paged K_rope cache --
+// float8_e4m3fn inputs with per-tensor fp32 scales, bf16 or fp32 output, fp32
+// accumulation, optional log-sum-exp output and merge with an earlier partial.
 // Semantics: page "flare_mla_prefill" (description; Parameters: q may be
 // float8_e4m3fn and the output is then bfloat16; the k_rope_scales overload);
 // every fp8 operand stands for code * scale of its tensor.
@@ -69,6 +70,9 @@ __device__ __forceinline__ i32x2 e4m3x4_to_bf16x4(int x) {
 
 }  // namespace
 
+// CAUSAL: causal mask, else the null mask.  PLAIN: bf16 output only (no
+// log-sum-exp, no earlier partial to merge).
+template <bool CAUSAL, bool PLAIN>
 __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
@@ -89,7 +93,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   const int32_t len = (int32_t)(a.cache_row_offsets[b + 1] - g0);
   const int32_t c0 = a.cache_offsets ? (int32_t)a.cache_offsets[b] : 0;
   const int32_t i_last = (int32_t)min(n, i0 + BM) - 1;
-  const int32_t jend = max(0, min(p + i_last - c0 + 1, len));
+  // causal: the keys some query of the tile can see, c0 + j <= p + i_last;
+  // null mask: every key the row holds for the sequence
+  constexpr bool causal = CAUSAL;
+  const int32_t jend = causal ? max(0, min(p + i_last - c0 + 1, len)) : len;
   const int32_t nkt = (jend + BN - 1) / BN;
 
   const int tid = threadIdx.x;
@@ -209,9 +216,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
     load_q();
     __builtin_amdgcn_sched_barrier(0);
     issue_rope(0, stage0, pg0);
-  } else {
-    load_q();
   }
+  // with no key to attend to, Q is never read (the epilogue writes 0, or passes
+  // an earlier partial through)
 
   auto step = [&](int32_t kt, const uint8_t* st, uint8_t* next) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -226,7 +233,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       pg_next = page_of(kt + 2);
     }
     const int32_t j0 = kt * BN;
-    if (!(wave_rows && c0 + j0 <= wq_last)) return;
+    if (!(wave_rows && (!causal || c0 + j0 <= wq_last))) return;
     // S^T: two nope k-steps, scale to rope units, one rope k-step
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -247,12 +254,12 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_fp8(kf[kb], qop[ks], s[kb]);
     }
-    const bool full = (j0 + BN <= len) && (c0 + j0 + BN - 1 <= wq_first);
+    const bool full = (j0 + BN <= len) && (!causal || c0 + j0 + BN - 1 <= wq_first);
     if (!full) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int32_t kbase = j0 + 32 * kb + 4 * hf;
-        const int32_t lim = min(len - 1 - kbase, p + my_i - c0 - kbase);
+        const int32_t lim = causal ? min(len - 1 - kbase, p + my_i - c0 - kbase) : len - 1 - kbase;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int32_t roff = 8 * (r >> 2) + (r & 3);
@@ -347,21 +354,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
     if (kt + 1 < nkt) step(kt + 1, stage1, stage0);
   }
 
-  // ---- epilogue: row sums of both halves, normalise, apply s_v, round to bf16
+  // ---- epilogue: row sums of both halves, normalise (applying s_v), store the
+  // row with its log-sum-exp (merged with an earlier partial when one is given)
   const float l_tot = l_run + swap_halves(l_run);
-  const float inv = l_tot > 0.f ? s_v / l_tot : 0.f;
   if (my_i < (int32_t)n) {
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(t0 + my_i) * H + h) * DV;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dv = d * 32 + g * 8 + hf * 4;
-        const uint32_t w0 = pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + dv) = u32x2{w0, w1};
-      }
-    }
+    const float inv = l_tot > 0.f ? s_v / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    store_output_row<PLAIN>(a, (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
   }
 }
 
@@ -370,7 +369,10 @@ hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream)
   const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles;
   const uint64_t grid = (units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_fp8_kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
+  const bool plain = !a.out_fp32 && !a.lse && !a.prev_out;
+  auto kernel = a.causal ? (plain ? prefill_fp8_kernel<true, true> : prefill_fp8_kernel<true, false>)
+                         : (plain ? prefill_fp8_kernel<false, true> : prefill_fp8_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,8 +1,14 @@
-"""One prefill step on the device: plan -> gather -> attention.
+"""One prefill step on the device: plan -> gather -> attention (-> merge).
 
 Holds a workload's tensors in device memory, allocates the plan, gather and
-output buffers once, and calls the three C entry points on the current
-stream.  No arithmetic of the method happens here.
+output buffers once, and calls the C entry points on the current stream.  No
+arithmetic of the method happens here.
+
+With a buffer-row capacity below the batch's context the plan makes several
+rows; each row's attention is a partial softmax over the keys the row holds,
+and the rows are combined through their log-sum-exps (the merge is fused into
+the attention's epilogue: row 0 writes an fp32 partial and its lse, later rows
+merge into it in place, the last one writes the bf16 output).
 """
 from __future__ import annotations
 
@@ -24,8 +30,9 @@ class PrefillStep:
     cache rows the gather copies (default: the whole row).
     """
 
-    def __init__(self, w: Workload, device="cuda", cap: int | None = None, gather_cols=None):
+    def __init__(self, w: Workload, device="cuda", cap: int | None = None, gather_cols=None, mask="causal"):
         self.w = w
+        self.mask = mask
         self.device = torch.device(device)
         dev = self.device
         self.fp8 = w.spec.dtype == "fp8"
@@ -54,6 +61,20 @@ class PrefillStep:
         self.gather_cols = (0, width) if gather_cols is None else tuple(gather_cols)
         self.gathered = torch.zeros((self.cap, self.gather_cols[1]), dtype=w.cache.dtype, device=dev)
         self.out = torch.zeros((w.total_q, w.heads, 128), dtype=torch.bfloat16, device=dev)
+        # fp32 partial and log-sum-exp carried between buffer rows
+        self.acc = None
+        self.lse = None
+        if self.rows > 1:
+            self.acc = torch.zeros((w.total_q, w.heads, 128), dtype=torch.float32, device=dev)
+            self.lse = torch.zeros((w.total_q, w.heads), dtype=torch.float32, device=dev)
+
+    def row_buffers(self, row: int):
+        """K_nope / V of plan row ``row``.  The workload's buffers hold every
+        sequence's context end to end in batch order (the one-row layout), and
+        row r covers positions [r * cap, r * cap + buffer_lengths[r]) of that
+        stream, so a row's buffer is a view at offset r * cap."""
+        lo = row * self.cap
+        return self.k_nope[lo:], self.v[lo:]
 
     def plan(self, stream=None):
         B.mla_prefill_plan(self.input_row_offsets, self.kv, self.w.spec.layer_idx, self.cap,
@@ -70,10 +91,32 @@ class PrefillStep:
         B.mla_prefill_ragged(self.out if out is None else out, self.q, self.k_nope if k_nope is None else k_nope,
                              self.v if v is None else v, self.kv, self.w.spec.layer_idx, self.input_row_offsets,
                              self.buffer_row_offsets[row], co, self.w.softmax_scale, sc.get("q"),
-                             sc.get("k_nope"), sc.get("v"), self.w.max_q, stream)
+                             sc.get("k_nope"), sc.get("v"), self.w.max_q, stream, mask=self.mask)
+
+    def attention_row_merged(self, row: int, stream=None):
+        """Attention over plan row ``row`` merged with rows 0 .. row-1 (rows > 1 only).
+
+        Row 0 writes the fp32 partial and its lse; a middle row merges into them
+        in place; the last row merges and writes the bf16 output."""
+        kn, v = self.row_buffers(row)
+        sc = self.scales or {}
+        last = row == self.rows - 1
+        first = row == 0
+        B.mla_prefill_ragged_lse(self.out if last else self.acc, None if last else self.lse, self.q, kn, v, self.kv,
+                                 self.w.spec.layer_idx, self.input_row_offsets, self.buffer_row_offsets[row],
+                                 self.cache_offsets[row], self.w.softmax_scale,
+                                 prev_output=None if first else self.acc, prev_lse=None if first else self.lse,
+                                 q_scale=sc.get("q"), k_nope_scale=sc.get("k_nope"), v_scale=sc.get("v"),
+                                 q_max_seq_len=self.w.max_q, stream=stream, mask=self.mask)
 
     def run(self, stream=None):
-        """The whole step: plan, gather of row 0, attention over row 0."""
+        """The whole step: plan, then per buffer row its gather and its attention
+        (merged across rows when there are several)."""
         self.plan(stream)
-        self.gather(0, stream)
-        self.attention(0, stream=stream)
+        if self.rows == 1:
+            self.gather(0, stream)
+            self.attention(0, stream=stream)
+            return
+        for r in range(self.rows):
+            self.gather(r, stream)
+            self.attention_row_merged(r, stream)

@@ -185,6 +185,18 @@ def causal_flops(n, p, heads: int) -> float:
     return 2.0 * heads * (Q_DEPTH + NOPE_DEPTH) * causal_pairs(n, p)
 
 
+def null_mask_pairs(n, p) -> int:
+    """(query, key) pairs under the null mask: every new token sees all of its sequence's keys."""
+    n = np.asarray(n, dtype=np.int64)
+    p = np.asarray(p, dtype=np.int64)
+    return int(np.sum(n * (n + p)))
+
+
+def null_mask_flops(n, p, heads: int) -> float:
+    """Algorithmic FLOPs under the null mask (same per-pair count as causal_flops)."""
+    return 2.0 * heads * (Q_DEPTH + NOPE_DEPTH) * null_mask_pairs(n, p)
+
+
 def algorithmic_bytes(w: Workload) -> float:
     """Bytes a prefill call must move at least once: Q, K_nope, V, K_rope in; O out (bf16)."""
     el = 1 if w.spec.dtype == "fp8" else 2

@@ -28,17 +28,30 @@ def check_plan(step, w):
     return bro, co, bl
 
 
-def oracle_full(w, bro_r, co_r, k_nope=None, v=None):
+def oracle_full(w, bro_r, co_r, k_nope=None, v=None, mask="causal", return_lse=False):
     return oracle.mla_prefill_ragged(w.q, w.k_nope if k_nope is None else k_nope, w.v if v is None else v, w.cache,
                                      w.spec.layer_idx, w.page_table, w.spec.page_size, w.spec.rope_col,
                                      w.cache_lengths, w.input_row_offsets, bro_r, co_r, w.softmax_scale,
-                                     scales=w.scales)
+                                     scales=w.scales, mask=mask, return_lse=return_lse)
 
 
-def oracle_rows(w, rows, bro_r, co_r):
+def oracle_rows(w, rows, bro_r, co_r, mask="causal", return_lse=False):
     return oracle.mla_prefill_rows(rows, w.q, w.k_nope, w.v, w.cache, w.spec.layer_idx, w.page_table,
                                    w.spec.page_size, w.spec.rope_col, w.cache_lengths, w.input_row_offsets,
-                                   bro_r, co_r, w.softmax_scale, scales=w.scales)
+                                   bro_r, co_r, w.softmax_scale, scales=w.scales, mask=mask, return_lse=return_lse)
+
+
+def report_lse(got, ref, bar, label):
+    """Compare log-sum-exps: -inf exactly where the oracle has -inf, else max abs error <= bar."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"[{label}] -inf pattern differs"
+    fin = np.isfinite(ref)
+    assert np.isfinite(got[fin]).all(), f"[{label}] non-finite lse where the oracle is finite"
+    worst = float(np.abs(got[fin] - ref[fin]).max()) if fin.any() else 0.0
+    say(f"[{label}] max|lse gpu-oracle| = {worst:.3e} (bar {bar:g}); finite = {int(fin.sum())}, "
+        f"-inf = {int((~fin).sum())}")
+    return worst
 
 
 def sample_rows(w, count, seed):

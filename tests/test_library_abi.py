@@ -28,8 +28,15 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_plan",
-                                    "mla_prefill_ragged", "mla_status_string"]
+    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_merge",
+                                    "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_lse",
+                                    "mla_status_string"]
+
+
+def test_binding_exposes_every_entry_point():
+    import mla_ragged_paged_amd as m
+    for name in declared_functions():
+        assert callable(getattr(m, name)), name
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -74,7 +81,7 @@ def test_validation_codes_without_gpu():
                          ctypes.c_float(0.07), kw.get("qs"), None, None, 0, None]
     assert lib.mla_prefill_ragged(*args(qd=576)) == 4
     assert lib.mla_prefill_ragged(*args(d=512)) == 4
-    assert lib.mla_prefill_ragged(*args(mask=1)) == 5
+    assert lib.mla_prefill_ragged(*args(mask=2)) == 5
     assert lib.mla_prefill_ragged(*args(odt=1)) == 3
     assert lib.mla_prefill_ragged(*args(qdt=1)) == 3        # cache dtype bf16 != q dtype
     assert lib.mla_prefill_ragged(*args(qs=dummy)) == 3     # scales given for bf16
@@ -85,3 +92,36 @@ def test_validation_codes_without_gpu():
     s.dtype = 1
     fp8 = args(qdt=1)
     assert lib.mla_prefill_ragged(*fp8) == 1                # fp8 needs every scale
+    s.dtype = 0
+
+
+def test_lse_and_merge_validation_without_gpu():
+    import mla_ragged_paged_amd._binding as b
+    lib = b._lib
+    dummy = ctypes.c_void_p(16)
+    s = b._Cache(data=16, dtype=0, num_layers=1, num_pages=1, page_size=16, row_width=64, rope_col=0,
+                 page_table=16, max_pages_per_seq=1, cache_lengths=16, scale=None)
+    ref = ctypes.byref(s)
+
+    def lse_args(**kw):
+        return [dummy, kw.get("odt", 2), kw.get("lse", dummy), kw.get("po"), kw.get("pl"), dummy, 0, dummy, dummy,
+                ref, 0, dummy, dummy, None, 1, 4, 2, 192, kw.get("d", 128), kw.get("mask", 1),
+                ctypes.c_float(0.07), None, None, None, 0, None]
+    assert lib.mla_prefill_ragged_lse(*lse_args(po=dummy)) == 1            # prev_output without prev_lse
+    assert lib.mla_prefill_ragged_lse(*lse_args(pl=dummy)) == 1            # prev_lse without prev_output
+    assert lib.mla_prefill_ragged_lse(*lse_args(odt=1)) == 3               # fp8 output
+    assert lib.mla_prefill_ragged_lse(*lse_args(mask=7)) == 5
+    assert lib.mla_prefill_ragged_lse(*lse_args(d=64)) == 4
+    assert lib.mla_prefill_ragged_lse(*lse_args(po=dummy, pl=ctypes.c_void_p(18))) == 2   # misaligned lse
+    assert lib.mla_prefill_ragged_lse(*lse_args(po=ctypes.c_void_p(24), pl=dummy)) == 2   # misaligned partial
+
+    def merge_args(**kw):
+        return [kw.get("out", dummy), kw.get("odt", 0), kw.get("lse"), kw.get("oa", dummy), dummy, dummy,
+                kw.get("lb", dummy), kw.get("t", 4), 2, kw.get("d", 128), None]
+    assert lib.mla_prefill_merge(*merge_args(out=None)) == 1
+    assert lib.mla_prefill_merge(*merge_args(lb=None)) == 1
+    assert lib.mla_prefill_merge(*merge_args(d=64)) == 4
+    assert lib.mla_prefill_merge(*merge_args(odt=1)) == 3
+    assert lib.mla_prefill_merge(*merge_args(oa=ctypes.c_void_p(20))) == 2
+    assert lib.mla_prefill_merge(*merge_args(lb=ctypes.c_void_p(18))) == 2
+    assert lib.mla_prefill_merge(*merge_args(t=0)) == 0                    # empty: a no-op
