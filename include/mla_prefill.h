@@ -20,6 +20,9 @@
  *   mla_prefill_ragged_lse  the same attention, also writing each (token, head)'s
  *                           log-sum-exp, optionally merged in place with the
  *                           partial result of earlier rows;
+ *   mla_prefill_ragged_row  one row of such a plan, rows run in order: each
+ *                           sequence's partial is carried in an fp32 accumulator
+ *                           from its first row to its last, which writes the output;
  *   mla_prefill_merge       log-sum-exp combine of two partial results.
  *
  * Conventions for every call:
@@ -250,6 +253,49 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
                                     const float* prev_output, const float* prev_lse,
                                     const void* q, mla_dtype_t qkv_dtype, const void* k_nope, const void* v,
                                     const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                    const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                    const uint32_t* cache_offsets, uint32_t batch_size,
+                                    uint32_t total_q_tokens, uint32_t num_heads, uint32_t q_depth,
+                                    uint32_t depth, mla_mask_t mask, float scale, const float* q_scale,
+                                    const float* k_nope_scale, const float* v_scale,
+                                    uint32_t q_max_seq_len, void* stream);
+
+/*
+ * mla_prefill_ragged_row -- one buffer row of the plan of page
+ * "generic_flare_mla_prefill_ragged_paged_plan" (description, Args: rows of
+ * fixed capacity, each sequence's slice given by its buffer_row_offsets and
+ * cache_offsets), when the plan cut the batch's contexts over several rows.
+ *
+ * All arguments from q on are those of mla_prefill_ragged, with the same
+ * meaning and checks; cache_row_offsets / cache_offsets must be row r of the
+ * plan (its buffer_row_offsets[r] and cache_offsets[r]) and k_nope / v that
+ * row's K/V buffer.  The call is made once per row, r = 0, 1, ..., in order on
+ * one stream, with the same acc / acc_lse for every row of the batch.  For a
+ * sequence b whose slice in this row is not empty, with len_b keys starting at
+ * cache position c_b = cache_offsets[b]:
+ *   c_b == 0 (b's first row)        the row's partial (output and lse as in
+ *                                   mla_prefill_ragged_lse) goes to acc / acc_lse;
+ *   neither first nor last          the row's partial is merged into acc / acc_lse;
+ *   c_b + len_b == kv->cache_lengths[b] + n_b (b's last row)
+ *                                   the row's partial is merged with acc / acc_lse
+ *                                   and the result goes to output (and lse);
+ *   first and last                  the row's result goes straight to output (and lse).
+ * A sequence with no keys in this row is not touched.  After the last row,
+ * output holds the attention over every key of every sequence (what
+ * mla_prefill_ragged computes over one row holding all of them), and lse, when
+ * given, its log-sum-exp.
+ *
+ *   output      device [total_q_tokens][num_heads][128], MLA_BF16 or MLA_FP32.
+ *   lse         device fp32 [total_q_tokens][num_heads] or NULL.
+ *   acc         device fp32 [total_q_tokens][num_heads][128], 16-byte aligned;
+ *               acc_lse device fp32 [total_q_tokens][num_heads].  Scratch owned by
+ *               the caller, carried between the rows of one batch; no initial
+ *               contents are needed.
+ * Errors: those of mla_prefill_ragged; NULL_ARG when acc or acc_lse is NULL.
+ */
+mla_status_t mla_prefill_ragged_row(void* output, mla_dtype_t output_dtype, float* lse, float* acc,
+                                    float* acc_lse, const void* q, mla_dtype_t qkv_dtype, const void* k_nope,
+                                    const void* v, const mla_paged_cache_t* k_rope, uint32_t layer_idx,
                                     const uint32_t* valid_length, const uint32_t* cache_row_offsets,
                                     const uint32_t* cache_offsets, uint32_t batch_size,
                                     uint32_t total_q_tokens, uint32_t num_heads, uint32_t q_depth,

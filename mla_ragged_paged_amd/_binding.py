@@ -67,6 +67,9 @@ def _load():
     lib.mla_prefill_ragged_lse.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32, u32,
                                            u32, u32, i32, ctypes.c_float, vp, vp, vp, u32, vp]
     lib.mla_prefill_ragged_lse.restype = i32
+    lib.mla_prefill_ragged_row.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32, u32,
+                                           u32, u32, i32, ctypes.c_float, vp, vp, vp, u32, vp]
+    lib.mla_prefill_ragged_row.restype = i32
     lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
     lib.mla_prefill_merge.restype = i32
     lib.mla_status_string.argtypes = [i32]
@@ -238,6 +241,25 @@ def mla_prefill_ragged_lse(output, lse, q, k_nope, v, k_rope: PagedCache, layer_
                                        k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
                                        _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
            "mla_prefill_ragged_lse")
+
+
+def mla_prefill_ragged_row(output, acc, acc_lse, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length,
+                           cache_row_offsets, cache_offsets, scale, lse=None, q_scale=None, k_nope_scale=None,
+                           v_scale=None, q_max_seq_len=0, stream=None, mask="causal"):
+    """One row of a multi-row plan (rows called in order): partials carried in acc fp32 [T, H, 128] /
+    acc_lse [T, H] from each sequence's first row to its last, which writes output (and lse)."""
+    T, H, qd = q.shape
+    _contiguous(output=output, lse=lse, acc=acc, acc_lse=acc_lse, q=q, k_nope=k_nope, v=v)
+    _shapes(T, H, rows=[("output", output), ("acc", acc)], lses=[("lse", lse), ("acc_lse", acc_lse)])
+    s = k_rope.as_struct()
+    _check(_lib.mla_prefill_ragged_row(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _f32(acc, "acc"),
+                                       _f32(acc_lse, "acc_lse"), _ptr(q), _dtype_code(q), _ptr(k_nope), _ptr(v),
+                                       ctypes.byref(s), layer_idx, _idx(valid_length, "valid_length"),
+                                       _idx(cache_row_offsets, "cache_row_offsets"),
+                                       _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H, qd,
+                                       k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
+                                       _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
+           "mla_prefill_ragged_row")
 
 
 def mla_prefill_merge(output, lse, o_a, lse_a, o_b, lse_b, stream=None):

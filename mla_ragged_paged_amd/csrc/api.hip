@@ -109,16 +109,22 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
   return hip_status(mla::launch_gather(a, unit, static_cast<hipStream_t>(stream)));
 }
 
-mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, float* lse, const float* prev_output,
-                                    const float* prev_lse, const void* q, mla_dtype_t qkv_dtype, const void* k_nope,
-                                    const void* v, const mla_paged_cache_t* k_rope, uint32_t layer_idx,
-                                    const uint32_t* valid_length, const uint32_t* cache_row_offsets,
-                                    const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
-                                    uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
-                                    float scale, const float* q_scale, const float* k_nope_scale,
-                                    const float* v_scale, uint32_t q_max_seq_len, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of the three attention entry points.
+mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, const float* prev_output,
+                          const float* prev_lse, float* acc, float* acc_lse, bool row_mode, const void* q,
+                          mla_dtype_t qkv_dtype, const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
+                          uint32_t layer_idx, const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                          const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                          uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
+                          const float* q_scale, const float* k_nope_scale, const float* v_scale,
+                          uint32_t q_max_seq_len, void* stream) {
   if (!output || !q || !k_nope || !v || !valid_length || !cache_row_offsets) return MLA_ERR_NULL_ARG;
   if ((prev_output == nullptr) != (prev_lse == nullptr)) return MLA_ERR_NULL_ARG;
+  if (row_mode && (!acc || !acc_lse)) return MLA_ERR_NULL_ARG;
   mla_status_t st = check_cache(k_rope, layer_idx);
   if (st != MLA_OK) return st;
   if (q_depth != 192 || depth != 128) return MLA_ERR_UNSUPPORTED_DIMS;
@@ -137,8 +143,9 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
     return MLA_ERR_BAD_SHAPE;
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_nope) | reinterpret_cast<uintptr_t>(v) |
        reinterpret_cast<uintptr_t>(k_rope->data) | reinterpret_cast<uintptr_t>(output) |
-       reinterpret_cast<uintptr_t>(prev_output)) % 16 ||
-      (reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(prev_lse)) % 4)
+       reinterpret_cast<uintptr_t>(prev_output) | reinterpret_cast<uintptr_t>(acc)) % 16 ||
+      (reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(prev_lse) |
+       reinterpret_cast<uintptr_t>(acc_lse)) % 4)
     return MLA_ERR_BAD_SHAPE;
   // the kernels address one sequence's rows and one cache layer with 32-bit byte offsets
   const uint64_t layer_bytes = (uint64_t)k_rope->num_pages * k_rope->page_size * k_rope->row_width * el;
@@ -153,6 +160,9 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
   a.lse = lse;
   a.prev_out = prev_output;
   a.prev_lse = prev_lse;
+  a.acc = acc;
+  a.acc_lse = acc_lse;
+  a.row_mode = row_mode ? 1u : 0u;
   a.out_fp32 = output_dtype == MLA_FP32 ? 1u : 0u;
   a.causal = mask == MLA_MASK_CAUSAL ? 1u : 0u;
   a.q = q;
@@ -187,6 +197,37 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
   return hip_status(mla::launch_prefill_bf16(a, q_max, s));
 }
 
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, float* lse, const float* prev_output,
+                                    const float* prev_lse, const void* q, mla_dtype_t qkv_dtype, const void* k_nope,
+                                    const void* v, const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                    const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                    const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                    uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
+                                    float scale, const float* q_scale, const float* k_nope_scale,
+                                    const float* v_scale, uint32_t q_max_seq_len, void* stream) {
+  return prefill_impl(output, output_dtype, lse, prev_output, prev_lse, nullptr, nullptr, false, q, qkv_dtype, k_nope,
+                      v, k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
+                      total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale,
+                      q_max_seq_len, stream);
+}
+
+mla_status_t mla_prefill_ragged_row(void* output, mla_dtype_t output_dtype, float* lse, float* acc, float* acc_lse,
+                                    const void* q, mla_dtype_t qkv_dtype, const void* k_nope, const void* v,
+                                    const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                    const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                    const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                    uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
+                                    float scale, const float* q_scale, const float* k_nope_scale,
+                                    const float* v_scale, uint32_t q_max_seq_len, void* stream) {
+  return prefill_impl(output, output_dtype, lse, nullptr, nullptr, acc, acc_lse, true, q, qkv_dtype, k_nope, v,
+                      k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size, total_q_tokens,
+                      num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream);
+}
+
 mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
                                 const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
                                 uint32_t layer_idx, const uint32_t* valid_length, const uint32_t* cache_row_offsets,
@@ -194,10 +235,10 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
                                 uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
                                 const float* q_scale, const float* k_nope_scale, const float* v_scale,
                                 uint32_t q_max_seq_len, void* stream) {
-  return mla_prefill_ragged_lse(output, output_dtype, nullptr, nullptr, nullptr, q, qkv_dtype, k_nope, v, k_rope,
-                                layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
-                                total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale,
-                                v_scale, q_max_seq_len, stream);
+  return prefill_impl(output, output_dtype, nullptr, nullptr, nullptr, nullptr, nullptr, false, q, qkv_dtype, k_nope,
+                      v, k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
+                      total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale,
+                      q_max_seq_len, stream);
 }
 
 mla_status_t mla_prefill_merge(void* output, mla_dtype_t output_dtype, float* lse, const float* o_a,

@@ -61,19 +61,43 @@ __device__ __forceinline__ MergeWeights merge_weights(float la, float lb) {
   return MergeWeights{ea / sum, eb / sum, mm + __builtin_amdgcn_logf(sum) * LN2_F};
 }
 
+// Where a unit's finished rows go: the output (bf16 or fp32), optionally the
+// log-sum-exp, optionally merged with an earlier partial.
+struct RowTarget {
+  void* out;
+  uint32_t out_fp32;
+  float* lse;
+  const float* prev;
+  const float* prev_lse;
+};
+
+// Target of one unit.  A plain call takes its own arguments.  In row mode (one
+// row of a plan that cut the contexts over several buffer rows, rows run in
+// order): sequence b's first row (its slice starts at cache position 0) starts
+// the fp32 partial in acc / acc_lse, a middle row merges into it in place, and
+// the last row (its slice ends at the context's end, p_b + n_b) merges and writes
+// the output; a sequence whose context one row holds writes the output directly.
+__device__ __forceinline__ RowTarget row_target(const PrefillArgs& a, bool first, bool last) {
+  if (!a.row_mode) return RowTarget{a.out, a.out_fp32, a.lse, a.prev_out, a.prev_lse};
+  if (first && last) return RowTarget{a.out, a.out_fp32, a.lse, nullptr, nullptr};
+  if (first) return RowTarget{a.acc, 1u, a.acc_lse, nullptr, nullptr};
+  if (!last) return RowTarget{a.acc, 1u, a.acc_lse, a.acc, a.acc_lse};
+  return RowTarget{a.out, a.out_fp32, a.lse, a.acc, a.acc_lse};
+}
+
 // Stores one lane's share of a finished query row (row = token * H + head).
 // o[d][4g + k] is output column 32d + 8g + 4hf + k before normalisation, `inv`
 // normalises it, and lse2 is the row's log-sum-exp in log2 units (-inf when the
-// call saw no key for the row).  With an earlier partial in a.prev_out /
-// a.prev_lse the two are combined by merge_weights; the earlier side is read
-// only where its weight is non-zero.  The output is written as bf16 (rounded
-// to nearest-even) or fp32, and the lower half's lanes store the
-// log-sum-exp, in natural-log units, when a.lse is set.  Each lane reads the
-// earlier partial's elements before it writes them, so out / lse may be the
-// same buffers as prev_out / prev_lse.
-// PLAIN: bf16 output, no log-sum-exp, no earlier partial (the fields are not read).
+// call saw no key for the row).  With an earlier partial in t.prev / t.prev_lse
+// the two are combined by merge_weights; the earlier side is read only where
+// its weight is non-zero.  The output is written as bf16 (rounded to
+// nearest-even) or fp32, and the lower half's lanes store the log-sum-exp, in
+// natural-log units, when t.lse is set.  Each lane reads the earlier partial's
+// elements before it writes them, so out / lse may be the same buffers as
+// prev / prev_lse.
+// PLAIN: bf16 output, no log-sum-exp, no earlier partial (only t.out is read).
 template <bool PLAIN>
-__device__ __forceinline__ void store_output_row(const PrefillArgs& a, size_t row, int hf, const f32x16 (&o)[4],
+__device__ __forceinline__ void store_output_row(const RowTarget& t, size_t row, int hf, const f32x16 (&o)[4],
                                                  float inv, float lse2) {
   if constexpr (PLAIN) {
 #pragma unroll
@@ -83,7 +107,7 @@ __device__ __forceinline__ void store_output_row(const PrefillArgs& a, size_t ro
         const int dv = d * 32 + g * 8 + hf * 4;
         const uint32_t w0 = pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv);
         const uint32_t w1 = pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * 128 + dv) = u32x2{w0, w1};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(t.out) + row * 128 + dv) = u32x2{w0, w1};
       }
     }
     return;
@@ -91,14 +115,14 @@ __device__ __forceinline__ void store_output_row(const PrefillArgs& a, size_t ro
   float w_self = inv, w_prev = 0.f;
   float lse = lse2 * LN2_F;
   const float* prev = nullptr;
-  if (a.prev_out) {
-    const MergeWeights mw = merge_weights(a.prev_lse[row], lse);
+  if (t.prev) {
+    const MergeWeights mw = merge_weights(t.prev_lse[row], lse);
     w_self = inv * mw.wb;
     w_prev = mw.wa;
     lse = mw.lse;
-    if (w_prev > 0.f) prev = a.prev_out + row * 128;
+    if (w_prev > 0.f) prev = t.prev + row * 128;
   }
-  if (a.lse && hf == 0) a.lse[row] = lse;
+  if (t.lse && hf == 0) t.lse[row] = lse;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -111,12 +135,12 @@ __device__ __forceinline__ void store_output_row(const PrefillArgs& a, size_t ro
         val = {__builtin_fmaf(w_prev, pv[0], val[0]), __builtin_fmaf(w_prev, pv[1], val[1]),
                __builtin_fmaf(w_prev, pv[2], val[2]), __builtin_fmaf(w_prev, pv[3], val[3])};
       }
-      if (a.out_fp32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * 128 + dv) = val;
+      if (t.out_fp32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(t.out) + row * 128 + dv) = val;
       } else {
         const uint32_t w0 = pack_bf16x2(val[0], val[1]);
         const uint32_t w1 = pack_bf16x2(val[2], val[3]);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * 128 + dv) = u32x2{w0, w1};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(t.out) + row * 128 + dv) = u32x2{w0, w1};
       }
     }
   }

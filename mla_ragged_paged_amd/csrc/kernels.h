@@ -65,6 +65,9 @@ struct PrefillArgs {
   uint32_t causal;                    // 1: key visible iff kpos <= qpos; 0: every key visible
   float scale;                        // softmax scale (its sign is applied to Q)
   float scale_log2;                   // max(|scale| * log2(e), 1e-30)
+  float* acc;                         // row mode: [T][H][128] fp32 partial carried between rows
+  float* acc_lse;                     // row mode: [T][H]
+  uint32_t row_mode;                  // 1: one plan row of several, called in row order
 };
 
 struct MergeArgs {

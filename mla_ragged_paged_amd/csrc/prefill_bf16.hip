@@ -97,6 +97,15 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const uint32_t g0 = a.cache_row_offsets[b];
   const int32_t len = (int32_t)(a.cache_row_offsets[b + 1] - g0);
   const int32_t c0 = a.cache_offsets ? (int32_t)a.cache_offsets[b] : 0;
+  // row mode: a row holding none of the sequence's keys leaves its outputs alone
+  bool row_first = true, row_last = true;
+  if constexpr (!PLAIN) {
+    if (a.row_mode) {
+      if (len == 0) return;
+      row_first = c0 == 0;
+      row_last = c0 + len == p + (int32_t)n;
+    }
+  }
   const int32_t i_last = (int32_t)min(n, i0 + BM) - 1;
   // causal: the keys some query of the tile can see, c0 + j <= p + i_last;
   // null mask: every key the row holds for the sequence
@@ -360,7 +369,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   if (my_i < (int32_t)n) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    store_output_row<PLAIN>(a, (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
+    store_output_row<PLAIN>(row_target(a, row_first, row_last), (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
   }
 }
 
@@ -369,7 +378,7 @@ hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream
   const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles;
   const uint64_t grid = (units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-  const bool plain = !a.out_fp32 && !a.lse && !a.prev_out;
+  const bool plain = !a.out_fp32 && !a.lse && !a.prev_out && !a.row_mode;
   auto kernel = a.causal ? (plain ? prefill_bf16_kernel<true, true> : prefill_bf16_kernel<true, false>)
                          : (plain ? prefill_bf16_kernel<false, true> : prefill_bf16_kernel<false, false>);
   hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);

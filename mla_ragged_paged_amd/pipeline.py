@@ -7,8 +7,9 @@ arithmetic of the method happens here.
 With a buffer-row capacity below the batch's context the plan makes several
 rows; each row's attention is a partial softmax over the keys the row holds,
 and the rows are combined through their log-sum-exps (the merge is fused into
-the attention's epilogue: row 0 writes an fp32 partial and its lse, later rows
-merge into it in place, the last one writes the bf16 output).
+the attention's epilogue: a sequence's first row writes an fp32 partial and its
+lse, its middle rows merge into them in place, its last row merges and writes
+the bf16 output).
 """
 from __future__ import annotations
 
@@ -94,20 +95,15 @@ class PrefillStep:
                              sc.get("k_nope"), sc.get("v"), self.w.max_q, stream, mask=self.mask)
 
     def attention_row_merged(self, row: int, stream=None):
-        """Attention over plan row ``row`` merged with rows 0 .. row-1 (rows > 1 only).
-
-        Row 0 writes the fp32 partial and its lse; a middle row merges into them
-        in place; the last row merges and writes the bf16 output."""
+        """Attention over plan row ``row`` of several (rows run in order): each
+        sequence's partial is carried in the fp32 accumulator from its first row
+        to its last, which writes the bf16 output."""
         kn, v = self.row_buffers(row)
         sc = self.scales or {}
-        last = row == self.rows - 1
-        first = row == 0
-        B.mla_prefill_ragged_lse(self.out if last else self.acc, None if last else self.lse, self.q, kn, v, self.kv,
-                                 self.w.spec.layer_idx, self.input_row_offsets, self.buffer_row_offsets[row],
-                                 self.cache_offsets[row], self.w.softmax_scale,
-                                 prev_output=None if first else self.acc, prev_lse=None if first else self.lse,
-                                 q_scale=sc.get("q"), k_nope_scale=sc.get("k_nope"), v_scale=sc.get("v"),
-                                 q_max_seq_len=self.w.max_q, stream=stream, mask=self.mask)
+        B.mla_prefill_ragged_row(self.out, self.acc, self.lse, self.q, kn, v, self.kv, self.w.spec.layer_idx,
+                                 self.input_row_offsets, self.buffer_row_offsets[row], self.cache_offsets[row],
+                                 self.w.softmax_scale, q_scale=sc.get("q"), k_nope_scale=sc.get("k_nope"),
+                                 v_scale=sc.get("v"), q_max_seq_len=self.w.max_q, stream=stream, mask=self.mask)
 
     def run(self, stream=None):
         """The whole step: plan, then per buffer row its gather and its attention

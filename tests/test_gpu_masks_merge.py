@@ -122,7 +122,10 @@ def test_rows_merged_every_output(mc, dtype, mask):
     say(f"rows merged {dtype} {mask} case {CASES[case]} cap {cap}")
     step = PrefillStep(w, "cuda", cap=cap, mask=mask)
     assert step.rows >= 2
+    # no initial contents are needed: every value read is written by an earlier row
     step.out.fill_(float("nan"))
+    step.acc.fill_(float("nan"))
+    step.lse.fill_(float("nan"))
     step.run()
     torch.cuda.synchronize()
     check_plan(step, w)
@@ -135,6 +138,64 @@ def test_rows_merged_every_output(mc, dtype, mask):
     step.run()
     torch.cuda.synchronize()
     assert torch.equal(first, step.out)
+
+
+@pytest.mark.parametrize("mask", ["causal", "null"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("mc", [0, 1, 3, 5])
+def test_rows_chained_through_the_lse_entry_point(mc, dtype, mask):
+    """The general entry point: row 0 writes an fp32 partial and lse, each later
+    row merges into them in place (prev = output), the last writes bf16."""
+    case, cap = MULTI[mc]["case"], MULTI[mc]["cap"]
+    w = _workload(case, dtype, 680)
+    step = PrefillStep(w, "cuda", cap=cap, mask=mask)
+    step.plan()
+    torch.cuda.synchronize()
+    check_plan(step, w)
+    acc = torch.full((w.total_q, w.heads, 128), float("nan"), device="cuda")
+    lse = torch.full((w.total_q, w.heads), float("nan"), device="cuda")
+    out = torch.full_like(step.out, float("nan"))
+    final_lse = torch.full_like(lse, float("nan"))
+    sc = step.scales or {}
+    for r in range(step.rows):
+        kn, v = step.row_buffers(r)
+        last = r == step.rows - 1
+        m.mla_prefill_ragged_lse(out if last else acc, final_lse if last else lse, step.q, kn, v, step.kv, 0,
+                                 step.input_row_offsets, step.buffer_row_offsets[r], step.cache_offsets[r],
+                                 w.softmax_scale, prev_output=None if r == 0 else acc,
+                                 prev_lse=None if r == 0 else lse, q_scale=sc.get("q"),
+                                 k_nope_scale=sc.get("k_nope"), v_scale=sc.get("v"), q_max_seq_len=w.max_q,
+                                 mask=mask)
+    torch.cuda.synchronize()
+    bro1, co1 = _one_row_plan(w)
+    ref, ref_lse = oracle_full(w, bro1, co1, mask=mask, return_lse=True)
+    assert report(out.float().cpu().numpy(), ref, BAR[dtype], f"chain-{dtype}-{mask}-{mc}") <= BAR[dtype]
+    assert report_lse(final_lse.cpu().numpy(), ref_lse, LSE_BAR[dtype], f"chain-lse-{dtype}-{mask}-{mc}") \
+        <= LSE_BAR[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_row_mode_final_lse_and_fp32_output(dtype):
+    """Row mode with the final log-sum-exp and an fp32 output."""
+    w = _workload(0, dtype, 690)
+    step = PrefillStep(w, "cuda", cap=120)
+    step.plan()
+    torch.cuda.synchronize()
+    check_plan(step, w)
+    out = torch.full((w.total_q, w.heads, 128), float("nan"), device="cuda")
+    lse = torch.full((w.total_q, w.heads), float("nan"), device="cuda")
+    sc = step.scales or {}
+    for r in range(step.rows):
+        kn, v = step.row_buffers(r)
+        m.mla_prefill_ragged_row(out, step.acc, step.lse, step.q, kn, v, step.kv, 0, step.input_row_offsets,
+                                 step.buffer_row_offsets[r], step.cache_offsets[r], w.softmax_scale, lse=lse,
+                                 q_scale=sc.get("q"), k_nope_scale=sc.get("k_nope"), v_scale=sc.get("v"),
+                                 q_max_seq_len=w.max_q)
+    torch.cuda.synchronize()
+    bro1, co1 = _one_row_plan(w)
+    ref, ref_lse = oracle_full(w, bro1, co1, return_lse=True)
+    assert report(out.cpu().numpy(), ref, BAR[dtype], f"rowmode-fp32-{dtype}") <= BAR[dtype]
+    assert report_lse(lse.cpu().numpy(), ref_lse, LSE_BAR[dtype], f"rowmode-lse-{dtype}") <= LSE_BAR[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_merge",
                                     "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_lse",
-                                    "mla_status_string"]
+                                    "mla_prefill_ragged_row", "mla_status_string"]
 
 
 def test_binding_exposes_every_entry_point():
@@ -114,6 +114,13 @@ def test_lse_and_merge_validation_without_gpu():
     assert lib.mla_prefill_ragged_lse(*lse_args(d=64)) == 4
     assert lib.mla_prefill_ragged_lse(*lse_args(po=dummy, pl=ctypes.c_void_p(18))) == 2   # misaligned lse
     assert lib.mla_prefill_ragged_lse(*lse_args(po=ctypes.c_void_p(24), pl=dummy)) == 2   # misaligned partial
+
+    def row_args(**kw):
+        return [dummy, 0, None, kw.get("acc", dummy), kw.get("acc_lse", dummy), dummy, 0, dummy, dummy, ref, 0,
+                dummy, dummy, None, 1, 4, 2, 192, 128, 0, ctypes.c_float(0.07), None, None, None, 0, None]
+    assert lib.mla_prefill_ragged_row(*row_args(acc=None)) == 1
+    assert lib.mla_prefill_ragged_row(*row_args(acc_lse=None)) == 1
+    assert lib.mla_prefill_ragged_row(*row_args(acc=ctypes.c_void_p(24))) == 2    # misaligned accumulator
 
     def merge_args(**kw):
         return [kw.get("out", dummy), kw.get("odt", 0), kw.get("lse"), kw.get("oa", dummy), dummy, dummy,
