@@ -22,6 +22,7 @@ from .mla_oracle import (  # noqa: F401
     rope_rows,
     mla_prefill_ragged,
     mla_prefill_rows,
+    mla_prefill_ragged_split,
     merge_partials,
     MASKS,
 )

@@ -42,6 +42,7 @@ __all__ = [
     "MASKS",
     "mla_prefill_ragged",
     "mla_prefill_rows",
+    "mla_prefill_ragged_split",
     "merge_partials",
 ]
 
@@ -414,3 +415,58 @@ def mla_prefill_ragged(q, k_nope, v, cache, layer_idx, page_table, page_size, ro
                 out[s0:s1, h, :], lse[s0:s1, h] = _attend(qb, kn, kr, vv, scale,
                                                           qpos_all[s0 - t0:s1 - t0], kpos, mask)
     return (out, lse) if return_lse else out
+
+
+def mla_prefill_ragged_split(q_nope, q_rope, k_nope, v, cache_lengths, valid_length, cache_row_offsets,
+                             cache_offsets, scale, k_rope_rows=None, cache=None, layer_idx=0, page_table=None,
+                             page_size=None, rope_col=None, scales=None, mask="causal", return_lse=False):
+    """Split-Q attention: "flare_mla_prefill", the overloads whose query comes in
+    two tensors, q_nope [T, H, 128] (with q_scale when fp8) and q_rope [T, H, 64],
+    and whose K carries k_scales; K_rope either paged (from the cache, as in
+    ``mla_prefill_ragged``) or contiguous.
+
+    Reading R-w: the score is the one of ``mla_prefill_ragged`` with the query's
+    columns 0..127 taken from q_nope and 128..191 from q_rope; q_rope is never
+    quantised (its type is not tied to q_nope's), so q_scale applies to q_nope
+    only.  ``scales`` (fp8 operands) = dict(q=, k_nope=, v=, k_rope=): q scales
+    q_nope, k_nope is the pages' k_scales (one fp32 per tensor, reading R-l),
+    k_rope the cache's scale (paged fp8 cache only).
+    Reading R-x: a contiguous K_rope ``k_rope_rows`` [rows, 1, 64] (or [rows, 64])
+    is laid out like K and V: key j of sequence b uses row
+    cache_row_offsets[b] + j.  Without it, K_rope comes from the paged cache.
+    Returns [T, H, 128] float64 (and lse [T, H] with ``return_lse``).
+    """
+    sc = scales or {}
+    fp8 = scales is not None
+    qn = _as_f64(q_nope, sc.get("q") if fp8 else None)
+    qr = _as_f64(q_rope)
+    q = np.concatenate([qn, qr], axis=2)
+    vl = np.asarray(valid_length, dtype=np.int64)
+    cro = np.asarray(cache_row_offsets, dtype=np.int64)
+    co = None if cache_offsets is None else np.asarray(cache_offsets, dtype=np.int64)
+    p = np.asarray(cache_lengths, dtype=np.int64)
+    B = vl.shape[0] - 1
+    T, H = int(q.shape[0]), int(q.shape[1])
+    out = np.zeros((T, H, NOPE_DEPTH), dtype=np.float64)
+    lse = np.full((T, H), -np.inf, dtype=np.float64)
+    contig = None
+    if k_rope_rows is not None:
+        contig = _as_f64(k_rope_rows).reshape(-1, ROPE_DEPTH)
+    for b in range(B):
+        t0, t1 = int(vl[b]), int(vl[b + 1])
+        if t1 == t0:
+            continue
+        g0, count = _sequence_keys(b, cro)
+        kpos = _key_positions(co, b, count)
+        if contig is not None:
+            kr = contig[g0:g0 + count]
+        else:
+            kr = _as_f64(rope_rows(cache, layer_idx, page_table, page_size, rope_col, b, kpos),
+                         sc.get("k_rope") if fp8 else None)
+        qpos = _query_positions(p, b, t1 - t0)
+        for h in range(H):
+            kn = _as_f64(k_nope[g0:g0 + count, h, :], sc.get("k_nope") if fp8 else None)
+            vv = _as_f64(v[g0:g0 + count, h, :], sc.get("v") if fp8 else None)
+            out[t0:t1, h, :], lse[t0:t1, h] = _attend(q[t0:t1, h, :], kn, kr, vv, scale, qpos, kpos, mask)
+    return (out, lse) if return_lse else out
+

@@ -9,6 +9,7 @@ import oracle.mla_oracle as om
 from tests import test_oracle_attention as A
 from tests import test_oracle_fp8 as F
 from tests import test_oracle_masks_merge as M
+from tests import test_oracle_split as S
 
 
 def _pins():
@@ -26,6 +27,11 @@ def _pins():
              M.test_lse_shift_by_constant_score, M.test_merge_two_single_key_partials_closed_form,
              M.test_merge_with_empty_side_is_identity, M.test_merge_is_symmetric_and_associative]
     pins += [lambda c=c: M.test_rows_merged_equal_single_row(c) for c in range(len(M.MULTI_ROW_CASES))]
+    pins += [lambda c=c, k=k: S.test_split_fp8_matches_brute_force(c, k)
+             for c in range(len(S.SPLIT_CASES)) for k in (False, True)]
+    pins += [lambda m=m: S.test_halves_of_one_query_equal_that_query(m) for m in ("causal", "null")]
+    pins += [S.test_q_scale_scales_q_nope_only, S.test_contiguous_rope_equals_paged_rope,
+             S.test_contiguous_rope_is_indexed_by_buffer_row]
     return pins
 
 
@@ -43,6 +49,7 @@ _orig_attend = om._attend
 _orig_visible = om._visible
 _orig_rope = om.rope_rows
 _orig_merge = om.merge_partials
+_orig_split = om.mla_prefill_ragged_split
 
 
 def _attend_no_rope(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
@@ -108,6 +115,37 @@ def _merge_swapped(o_a, lse_a, o_b, lse_b):
     return wa[..., None] * o_a + wb[..., None] * o_b, lse
 
 
+def _split_q_scale_on_rope(q_nope, q_rope, *args, scales=None, **kw):
+    if scales is not None:
+        q_rope = np.asarray(om._as_f64(q_rope)) * scales["q"]
+    return _orig_split(q_nope, q_rope, *args, scales=scales, **kw)
+
+
+def _split_rope_ignored(q_nope, q_rope, *args, **kw):
+    return _orig_split(q_nope, np.zeros_like(np.asarray(om._as_f64(q_rope))), *args, **kw)
+
+
+def _split_contig_by_position(q_nope, q_rope, k_nope, v, cache_lengths, valid_length, cache_row_offsets,
+                              cache_offsets, scale, k_rope_rows=None, **kw):
+    if k_rope_rows is not None:
+        rows = np.asarray(om._as_f64(k_rope_rows)).reshape(-1, 64)
+        moved = np.zeros_like(rows)
+        cro = np.asarray(cache_row_offsets, dtype=np.int64)
+        for b in range(len(cro) - 1):
+            c0 = 0 if cache_offsets is None else int(cache_offsets[b])
+            for j in range(int(cro[b + 1] - cro[b])):
+                moved[cro[b] + j] = rows[min(c0 + j, len(rows) - 1)]
+        k_rope_rows = moved
+    return _orig_split(q_nope, q_rope, k_nope, v, cache_lengths, valid_length, cache_row_offsets, cache_offsets,
+                       scale, k_rope_rows=k_rope_rows, **kw)
+
+
+def _split_k_rope_scale_dropped(*args, scales=None, **kw):
+    if scales is not None:
+        scales = dict(scales, k_rope=1.0)
+    return _orig_split(*args, scales=scales, **kw)
+
+
 def _rope_logical_pages(cache, layer_idx, page_table, page_size, rope_col, b, positions):
     pt = np.asarray(om._host_array(page_table)).copy()
     pt[b] = np.arange(pt.shape[1])
@@ -141,6 +179,10 @@ MUTATIONS = {
     "merge by plain average": ("merge_partials", _merge_plain_average),
     "merge by the larger lse only": ("merge_partials", _merge_max_only),
     "merge weights swapped": ("merge_partials", _merge_swapped),
+    "split: q_scale applied to q_rope too": ("mla_prefill_ragged_split", _split_q_scale_on_rope),
+    "split: q_rope ignored": ("mla_prefill_ragged_split", _split_rope_ignored),
+    "split: contiguous rope indexed by position": ("mla_prefill_ragged_split", _split_contig_by_position),
+    "split: cache scale of K_rope dropped": ("mla_prefill_ragged_split", _split_k_rope_scale_dropped),
     "mask ignores the prefix": ("_query_positions", lambda p, b, count: np.arange(count, dtype=np.int64)),
     "cache_offsets ignored": ("_key_positions", lambda co, b, count: np.arange(count, dtype=np.int64)),
     "page table ignored": ("rope_rows", _rope_logical_pages),
