@@ -166,8 +166,9 @@ def _median_ms(torch, fn, reps, stream):
 def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
     """The paths beside the headline step, on the same workload:
     the null mask (every key visible), the context cut into three buffer rows
-    whose partials merge in the attention epilogue, and the standalone merge
-    kernel's bandwidth on fp32 partials."""
+    whose partials merge in the attention epilogue, the split-query calls (also
+    on the fp8 workload), and the standalone merge kernel's bandwidth on fp32
+    partials."""
     from mla_ragged_paged_amd import _binding as B
     from mla_ragged_paged_amd import workloads
     from mla_ragged_paged_amd.pipeline import PrefillStep
@@ -200,6 +201,35 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
                           "frac_of_peak": round(fl / (attn_med * 1e-3) / 1e12 / peak, 4),
                           "attention_time_vs_one_row": round(attn_med / one_row_attention_ms, 3)}
     del mr
+
+    # split query: bf16 on this workload (contiguous K_rope rows), and the fp8
+    # workload's e4m3 q_nope / K / V with a bf16 q_rope, K_rope from its e4m3 cache
+    # and from contiguous bf16 rows
+    out["split_q"] = {}
+    for wl in ([w] + ([workloads.build(workloads.SPECS["fp8"])] if w.spec.dtype == "bf16" else [])):
+        st = PrefillStep(wl, "cuda:0")
+        st.plan()
+        q_nope, q_rope = workloads.split_query(wl)
+        q_nope, q_rope = q_nope.to("cuda:0"), q_rope.to("cuda:0")
+        rows = workloads.draw_rope_rows(wl.total_ctx, seed=wl.spec.seed).to("cuda:0")
+        o = torch.empty((wl.total_q, wl.heads, 128), dtype=torch.bfloat16, device="cuda:0")
+        sc = st.scales or {}
+        fl = workloads.causal_flops(wl.n, wl.p, wl.heads)
+        pk = PEAK_TFLOPS[wl.spec.dtype]
+        for rope in (["paged", "contiguous"] if wl.spec.dtype == "fp8" else ["contiguous"]):
+            def call():
+                B.mla_prefill_ragged_split(o, q_nope, q_rope, st.k_nope, st.v, st.kv, 0, st.input_row_offsets,
+                                           st.buffer_row_offsets[0], st.cache_offsets[0], wl.softmax_scale,
+                                           q_scale=sc.get("q"), k_scales=sc.get("k_nope"), v_scale=sc.get("v"),
+                                           k_rope_rows=rows if rope == "contiguous" else None,
+                                           q_max_seq_len=wl.max_q)
+            call()
+            med, best = _median_ms(torch, call, reps, stream)
+            out["split_q"][f"{wl.spec.name}_{rope}_rope"] = {
+                "dtype": wl.spec.dtype, "attention_median_ms": round(med, 4), "attention_min_ms": round(best, 4),
+                "achieved_TFLOPs": round(fl / (med * 1e-3) / 1e12, 2),
+                "frac_of_peak": round(fl / (med * 1e-3) / 1e12 / pk, 4)}
+        del st
 
     T, H = 16384, 128
     dev = torch.device("cuda:0")

@@ -14,6 +14,11 @@
  *                       "flare_mla_prefill"; launch shape and argument meanings
  *                       of page "mla_prefill_v2_ragged").
  *
+ *   mla_prefill_ragged_split  the same attention for a query given in two parts,
+ *                       q_nope and q_rope, and K_rope from the cache or from
+ *                       contiguous rows (page "flare_mla_prefill", the q_nope /
+ *                       q_rope / q_scale / k_scales overloads).
+ *
  * When the plan cuts the contexts over several buffer rows, each row's
  * attention covers part of a sequence's keys:
  *
@@ -259,6 +264,47 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
                                     uint32_t depth, mla_mask_t mask, float scale, const float* q_scale,
                                     const float* k_nope_scale, const float* v_scale,
                                     uint32_t q_max_seq_len, void* stream);
+
+/*
+ * mla_prefill_ragged_split -- page "flare_mla_prefill", the overloads whose query
+ * is split into q_nope (element type `dtype`, with q_scale) and q_rope, whose K
+ * carries k_scales, and whose k_rope is either the paged cache or a plain tensor.
+ *
+ * The attention of mla_prefill_ragged with q[t][h][0..127] = q_nope[t][h][:] and
+ * q[t][h][128..191] = q_rope[t][h][:], where:
+ *   q_nope        device [total_q_tokens][num_heads][128], qkv_dtype; fp8 values
+ *                 stand for code * (*q_scale).
+ *   q_rope        device [total_q_tokens][num_heads][64], bf16, never scaled.
+ *   k_nope, v     device [rows][num_heads][128], qkv_dtype; fp8: code * (*k_scales)
+ *                 and code * (*v_scale) (one fp32 per tensor).
+ *   k_rope_rows   contiguous K_rope, device bf16 [rows][1][64] laid out like k_nope:
+ *                 key j of sequence b uses row cache_row_offsets[b] + j.  NULL:
+ *                 K_rope comes from the paged cache `kv` as in mla_prefill_ragged
+ *                 (a bf16 cache, or an e4m3 cache with kv->scale when qkv_dtype is
+ *                 MLA_FP8_E4M3FN; e4m3 K_rope is converted exactly to bf16 for its
+ *                 product with q_rope).
+ *   kv            [host] cache descriptor.  With k_rope_rows only kv->cache_lengths
+ *                 (the start positions) is read.
+ *   q_scale, k_scales, v_scale  device fp32 scalars, required for MLA_FP8_E4M3FN
+ *                 and NULL for MLA_BF16.
+ * Other arguments as in mla_prefill_ragged; depth must be 128.  output is bf16
+ * or fp32; lse (fp32 [total_q_tokens][num_heads] or NULL) receives each (token,
+ * head)'s log-sum-exp as in mla_prefill_ragged_lse.  The score is
+ *   s_j = scale * ( q_nope . k_nope + q_rope . K_rope )  on the dequantised values.
+ * Errors: NULL_ARG (q_rope, required scales, kv->cache_lengths), BAD_SHAPE
+ * (16-byte alignment of q_nope, q_rope, k_rope_rows, k_nope, v, output),
+ * UNSUPPORTED_DTYPE (bf16 q_nope with an e4m3 cache, scales given for bf16),
+ * UNSUPPORTED_DIMS, UNSUPPORTED_MASK, HIP.
+ */
+mla_status_t mla_prefill_ragged_split(void* output, mla_dtype_t output_dtype, float* lse, const void* q_nope,
+                                      const void* q_rope, mla_dtype_t qkv_dtype, const float* q_scale,
+                                      const void* k_nope, const float* k_scales, const void* v,
+                                      const float* v_scale, const void* k_rope_rows, const mla_paged_cache_t* kv,
+                                      uint32_t layer_idx, const uint32_t* valid_length,
+                                      const uint32_t* cache_row_offsets, const uint32_t* cache_offsets,
+                                      uint32_t batch_size, uint32_t total_q_tokens, uint32_t num_heads,
+                                      uint32_t depth, mla_mask_t mask, float scale, uint32_t q_max_seq_len,
+                                      void* stream);
 
 /*
  * mla_prefill_ragged_row -- one buffer row of the plan of page

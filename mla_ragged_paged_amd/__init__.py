@@ -23,5 +23,6 @@ from ._binding import (  # noqa: F401
     mla_prefill_ragged,
     mla_prefill_ragged_lse,
     mla_prefill_ragged_row,
+    mla_prefill_ragged_split,
     mla_status_string,
 )

@@ -70,6 +70,9 @@ def _load():
     lib.mla_prefill_ragged_row.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32, u32,
                                            u32, u32, i32, ctypes.c_float, vp, vp, vp, u32, vp]
     lib.mla_prefill_ragged_row.restype = i32
+    lib.mla_prefill_ragged_split.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, cp, u32, vp, vp, vp,
+                                             u32, u32, u32, u32, i32, ctypes.c_float, u32, vp]
+    lib.mla_prefill_ragged_split.restype = i32
     lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
     lib.mla_prefill_merge.restype = i32
     lib.mla_status_string.argtypes = [i32]
@@ -260,6 +263,35 @@ def mla_prefill_ragged_row(output, acc, acc_lse, q, k_nope, v, k_rope: PagedCach
                                        k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
                                        _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
            "mla_prefill_ragged_row")
+
+
+def mla_prefill_ragged_split(output, q_nope, q_rope, k_nope, v, kv: PagedCache, layer_idx, valid_length,
+                             cache_row_offsets, cache_offsets, scale, q_scale=None, k_scales=None, v_scale=None,
+                             k_rope_rows=None, lse=None, q_max_seq_len=0, stream=None, mask="causal"):
+    """Split-query attention: q_nope [T, H, 128] (bf16 or fp8 with q_scale), q_rope [T, H, 64] bf16;
+    K_rope from ``kv`` (paged) or from contiguous bf16 rows ``k_rope_rows`` [rows, 1, 64]."""
+    T, H, qd = q_nope.shape
+    _contiguous(output=output, lse=lse, q_nope=q_nope, q_rope=q_rope, k_nope=k_nope, v=v, k_rope_rows=k_rope_rows)
+    _shapes(T, H, rows=[("output", output)], lses=[("lse", lse)])
+    if tuple(q_rope.shape) != (T, H, 64) or q_rope.dtype != torch.bfloat16:
+        raise ValueError(f"q_rope must be bf16 of shape {(T, H, 64)}")
+    if k_rope_rows is not None and (k_rope_rows.dtype != torch.bfloat16 or k_rope_rows.shape[-1] != 64):
+        raise ValueError("k_rope_rows must be bf16 [rows, 1, 64]")
+    if k_rope_rows is not None:
+        s = _Cache(data=None, dtype=_dtype_code(q_nope), num_layers=0, num_pages=0, page_size=0, row_width=0,
+                   rope_col=0, page_table=None, max_pages_per_seq=0,
+                   cache_lengths=_idx(kv.cache_lengths, "cache_lengths").value, scale=None)
+    else:
+        s = kv.as_struct()
+    _check(_lib.mla_prefill_ragged_split(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _ptr(q_nope),
+                                         _ptr(q_rope), _dtype_code(q_nope), _ptr(q_scale), _ptr(k_nope),
+                                         _ptr(k_scales), _ptr(v), _ptr(v_scale), _ptr(k_rope_rows),
+                                         ctypes.byref(s), layer_idx, _idx(valid_length, "valid_length"),
+                                         _idx(cache_row_offsets, "cache_row_offsets"),
+                                         _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H,
+                                         k_nope.shape[2], _mask_code(mask), float(scale), int(q_max_seq_len),
+                                         _stream(stream)),
+           "mla_prefill_ragged_split")
 
 
 def mla_prefill_merge(output, lse, o_a, lse_a, o_b, lse_b, stream=None):

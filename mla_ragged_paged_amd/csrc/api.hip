@@ -113,43 +113,75 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
 
 namespace {
 
-// Shared validation and launch of the three attention entry points.
+// Query and K_rope sources of a call: one q [T][H][192] and K_rope from the
+// paged cache, or (split) q_nope [T][H][128] + bf16 q_rope [T][H][64] with K_rope
+// from the paged cache or from contiguous bf16 rows laid out like K.
+struct QuerySource {
+  const void* q;           // q, or q_nope when split
+  const void* q_rope;      // split only
+  const void* rope_rows;   // split only, may be NULL (paged)
+  bool split;
+};
+
+// Shared validation and launch of the attention entry points.
 mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, const float* prev_output,
-                          const float* prev_lse, float* acc, float* acc_lse, bool row_mode, const void* q,
+                          const float* prev_lse, float* acc, float* acc_lse, bool row_mode, const QuerySource& qs,
                           mla_dtype_t qkv_dtype, const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
                           uint32_t layer_idx, const uint32_t* valid_length, const uint32_t* cache_row_offsets,
                           const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
                           uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
                           const float* q_scale, const float* k_nope_scale, const float* v_scale,
                           uint32_t q_max_seq_len, void* stream) {
-  if (!output || !q || !k_nope || !v || !valid_length || !cache_row_offsets) return MLA_ERR_NULL_ARG;
+  if (!output || !qs.q || !k_nope || !v || !valid_length || !cache_row_offsets) return MLA_ERR_NULL_ARG;
+  if (qs.split && !qs.q_rope) return MLA_ERR_NULL_ARG;
   if ((prev_output == nullptr) != (prev_lse == nullptr)) return MLA_ERR_NULL_ARG;
   if (row_mode && (!acc || !acc_lse)) return MLA_ERR_NULL_ARG;
-  mla_status_t st = check_cache(k_rope, layer_idx);
-  if (st != MLA_OK) return st;
-  if (q_depth != 192 || depth != 128) return MLA_ERR_UNSUPPORTED_DIMS;
+  const bool contig = qs.split && qs.rope_rows != nullptr;
+  if (contig) {
+    // K_rope rows are given; the cache descriptor supplies the start positions only
+    if (!k_rope || !k_rope->cache_lengths) return MLA_ERR_NULL_ARG;
+  } else {
+    mla_status_t st = check_cache(k_rope, layer_idx);
+    if (st != MLA_OK) return st;
+  }
+  if (q_depth != (qs.split ? 128u : 192u) || depth != 128) return MLA_ERR_UNSUPPORTED_DIMS;
   if (mask != MLA_MASK_CAUSAL && mask != MLA_MASK_NULL) return MLA_ERR_UNSUPPORTED_MASK;
-  if (!dtype_known(qkv_dtype) || (output_dtype != MLA_BF16 && output_dtype != MLA_FP32) ||
-      k_rope->dtype != qkv_dtype)
+  if (!dtype_known(qkv_dtype) || (output_dtype != MLA_BF16 && output_dtype != MLA_FP32))
     return MLA_ERR_UNSUPPORTED_DTYPE;
   const bool fp8 = qkv_dtype == MLA_FP8_E4M3FN;
-  if (fp8 && (!q_scale || !k_nope_scale || !v_scale || !k_rope->scale)) return MLA_ERR_NULL_ARG;
+  // K_rope's type: the cache's (it must match q's for a full query; a split query
+  // takes a bf16 cache, or an e4m3 one with e4m3 q_nope), bf16 for contiguous rows
+  const bool rope_fp8 = !contig && k_rope->dtype == MLA_FP8_E4M3FN;
+  if (!contig) {
+    if (!qs.split && k_rope->dtype != qkv_dtype) return MLA_ERR_UNSUPPORTED_DTYPE;
+    if (qs.split && rope_fp8 && !fp8) return MLA_ERR_UNSUPPORTED_DTYPE;
+  }
+  if (fp8 && (!q_scale || !k_nope_scale || !v_scale)) return MLA_ERR_NULL_ARG;
+  if (rope_fp8 && !k_rope->scale) return MLA_ERR_NULL_ARG;
   if (!fp8 && (q_scale || k_nope_scale || v_scale)) return MLA_ERR_UNSUPPORTED_DTYPE;
   if (batch_size == 0 || total_q_tokens == 0) return MLA_OK;
   if (num_heads == 0) return MLA_ERR_BAD_SHAPE;
-  // 16-byte row segments: the rope window and rows must start on 16-byte boundaries
   const uint32_t el = (uint32_t)dtype_bytes(qkv_dtype);
-  if ((k_rope->rope_col * el) % 16 || (k_rope->row_width * el) % 16 || (uint64_t)k_rope->rope_col + 64 > k_rope->row_width)
-    return MLA_ERR_BAD_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_nope) | reinterpret_cast<uintptr_t>(v) |
-       reinterpret_cast<uintptr_t>(k_rope->data) | reinterpret_cast<uintptr_t>(output) |
+  uint64_t layer_bytes = 0;
+  if (!contig) {
+    // 16-byte row segments: the rope window and rows must start on 16-byte boundaries
+    const uint32_t rel = (uint32_t)dtype_bytes(k_rope->dtype);
+    if ((k_rope->rope_col * rel) % 16 || (k_rope->row_width * rel) % 16 ||
+        (uint64_t)k_rope->rope_col + 64 > k_rope->row_width)
+      return MLA_ERR_BAD_SHAPE;
+    layer_bytes = (uint64_t)k_rope->num_pages * k_rope->page_size * k_rope->row_width * rel;
+    if (reinterpret_cast<uintptr_t>(k_rope->data) % 16) return MLA_ERR_BAD_SHAPE;
+  }
+  if ((reinterpret_cast<uintptr_t>(qs.q) | reinterpret_cast<uintptr_t>(qs.q_rope) |
+       reinterpret_cast<uintptr_t>(qs.rope_rows) | reinterpret_cast<uintptr_t>(k_nope) |
+       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(output) |
        reinterpret_cast<uintptr_t>(prev_output) | reinterpret_cast<uintptr_t>(acc)) % 16 ||
       (reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(prev_lse) |
        reinterpret_cast<uintptr_t>(acc_lse)) % 4)
     return MLA_ERR_BAD_SHAPE;
   // the kernels address one sequence's rows and one cache layer with 32-bit byte offsets
-  const uint64_t layer_bytes = (uint64_t)k_rope->num_pages * k_rope->page_size * k_rope->row_width * el;
-  if (layer_bytes >= (1ull << 32) || (uint64_t)total_q_tokens * num_heads * q_depth * el >= (1ull << 32))
+  if (layer_bytes >= (1ull << 32) || (uint64_t)total_q_tokens * num_heads * q_depth * el >= (1ull << 32) ||
+      (qs.split && (uint64_t)total_q_tokens * num_heads * 64 * 2 >= (1ull << 32)))
     return MLA_ERR_BAD_SHAPE;
   const uint32_t q_max = q_max_seq_len ? q_max_seq_len : total_q_tokens;
   const uint64_t units = (uint64_t)num_heads * batch_size * ((q_max + 127) / 128);
@@ -165,29 +197,35 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
   a.row_mode = row_mode ? 1u : 0u;
   a.out_fp32 = output_dtype == MLA_FP32 ? 1u : 0u;
   a.causal = mask == MLA_MASK_CAUSAL ? 1u : 0u;
-  a.q = q;
+  a.q = qs.q;
+  a.q_rope = qs.q_rope;
+  a.rope_rows = qs.rope_rows;
+  // 0: full query; 1: split, e4m3 K_rope from the cache; 2: split, bf16 K_rope
+  a.q_split = !qs.split ? 0u : rope_fp8 ? 1u : 2u;
   a.k_nope = k_nope;
   a.v = v;
-  a.cache = layer_base(k_rope, layer_idx);
-  a.page_table = k_rope->page_table;
   a.cache_lengths = k_rope->cache_lengths;
+  if (!contig) {
+    a.cache = layer_base(k_rope, layer_idx);
+    a.page_table = k_rope->page_table;
+    a.k_rope_scale = k_rope->scale;
+    a.max_pages = k_rope->max_pages_per_seq;
+    a.page_size = k_rope->page_size;
+    a.page_shift = (k_rope->page_size & (k_rope->page_size - 1)) == 0 ? (uint32_t)__builtin_ctz(k_rope->page_size)
+                                                                        : 0xFFFFFFFFu;
+    a.row_width = k_rope->row_width;
+    a.rope_col = k_rope->rope_col;
+    a.cache_bytes = (uint32_t)layer_bytes;
+  }
   a.valid_length = valid_length;
   a.cache_row_offsets = cache_row_offsets;
   a.cache_offsets = cache_offsets;
   a.q_scale = q_scale;
   a.k_nope_scale = k_nope_scale;
   a.v_scale = v_scale;
-  a.k_rope_scale = k_rope->scale;
-  a.max_pages = k_rope->max_pages_per_seq;
-  a.page_size = k_rope->page_size;
-  a.page_shift = (k_rope->page_size & (k_rope->page_size - 1)) == 0 ? (uint32_t)__builtin_ctz(k_rope->page_size)
-                                                                      : 0xFFFFFFFFu;
-  a.row_width = k_rope->row_width;
-  a.rope_col = k_rope->rope_col;
   a.batch = batch_size;
   a.heads = num_heads;
   a.scale = scale;
-  a.cache_bytes = (uint32_t)layer_bytes;
   {
     const float c = (scale < 0.f ? -scale : scale) * 1.4426950408889634f;
     a.scale_log2 = c > 1e-30f ? c : 1e-30f;  // scale 0: every visible key weighs the same
@@ -209,7 +247,8 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
                                     uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
                                     float scale, const float* q_scale, const float* k_nope_scale,
                                     const float* v_scale, uint32_t q_max_seq_len, void* stream) {
-  return prefill_impl(output, output_dtype, lse, prev_output, prev_lse, nullptr, nullptr, false, q, qkv_dtype, k_nope,
+  return prefill_impl(output, output_dtype, lse, prev_output, prev_lse, nullptr, nullptr, false,
+                      QuerySource{q, nullptr, nullptr, false}, qkv_dtype, k_nope,
                       v, k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
                       total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale,
                       q_max_seq_len, stream);
@@ -223,7 +262,8 @@ mla_status_t mla_prefill_ragged_row(void* output, mla_dtype_t output_dtype, floa
                                     uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
                                     float scale, const float* q_scale, const float* k_nope_scale,
                                     const float* v_scale, uint32_t q_max_seq_len, void* stream) {
-  return prefill_impl(output, output_dtype, lse, nullptr, nullptr, acc, acc_lse, true, q, qkv_dtype, k_nope, v,
+  return prefill_impl(output, output_dtype, lse, nullptr, nullptr, acc, acc_lse, true,
+                      QuerySource{q, nullptr, nullptr, false}, qkv_dtype, k_nope, v,
                       k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size, total_q_tokens,
                       num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream);
 }
@@ -235,10 +275,26 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
                                 uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
                                 const float* q_scale, const float* k_nope_scale, const float* v_scale,
                                 uint32_t q_max_seq_len, void* stream) {
-  return prefill_impl(output, output_dtype, nullptr, nullptr, nullptr, nullptr, nullptr, false, q, qkv_dtype, k_nope,
+  return prefill_impl(output, output_dtype, nullptr, nullptr, nullptr, nullptr, nullptr, false,
+                      QuerySource{q, nullptr, nullptr, false}, qkv_dtype, k_nope,
                       v, k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
                       total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale,
                       q_max_seq_len, stream);
+}
+
+mla_status_t mla_prefill_ragged_split(void* output, mla_dtype_t output_dtype, float* lse, const void* q_nope,
+                                      const void* q_rope, mla_dtype_t qkv_dtype, const float* q_scale,
+                                      const void* k_nope, const float* k_scales, const void* v,
+                                      const float* v_scale, const void* k_rope_rows, const mla_paged_cache_t* kv,
+                                      uint32_t layer_idx, const uint32_t* valid_length,
+                                      const uint32_t* cache_row_offsets, const uint32_t* cache_offsets,
+                                      uint32_t batch_size, uint32_t total_q_tokens, uint32_t num_heads,
+                                      uint32_t depth, mla_mask_t mask, float scale, uint32_t q_max_seq_len,
+                                      void* stream) {
+  return prefill_impl(output, output_dtype, lse, nullptr, nullptr, nullptr, nullptr, false,
+                      QuerySource{q_nope, q_rope, k_rope_rows, true}, qkv_dtype, k_nope, v, kv, layer_idx,
+                      valid_length, cache_row_offsets, cache_offsets, batch_size, total_q_tokens, num_heads, 128,
+                      depth, mask, scale, q_scale, k_scales, v_scale, q_max_seq_len, stream);
 }
 
 mla_status_t mla_prefill_merge(void* output, mla_dtype_t output_dtype, float* lse, const float* o_a,

@@ -68,6 +68,9 @@ struct PrefillArgs {
   float* acc;                         // row mode: [T][H][128] fp32 partial carried between rows
   float* acc_lse;                     // row mode: [T][H]
   uint32_t row_mode;                  // 1: one plan row of several, called in row order
+  const void* q_rope;                 // split Q: bf16 [T][H][64] (q then holds q_nope [T][H][128])
+  const void* rope_rows;              // contiguous bf16 K_rope [rows][64] laid out like K, or nullptr (paged)
+  uint32_t q_split;                   // 1: Q comes as q_nope (a.q) + q_rope
 };
 
 struct MergeArgs {

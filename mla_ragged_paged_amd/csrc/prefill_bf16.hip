@@ -77,8 +77,10 @@ __device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, uint32_t off
 }  // namespace
 
 // CAUSAL: causal mask, else the null mask.  PLAIN: bf16 output only (no
-// log-sum-exp, no earlier partial to merge).
-template <bool CAUSAL, bool PLAIN>
+// log-sum-exp, no earlier partial to merge).  QSPLIT: the query comes as q_nope
+// [T][H][128] and q_rope [T][H][64], and K_rope may be given as contiguous rows
+// laid out like K (else it is read through the page table).
+template <bool CAUSAL, bool PLAIN, bool QSPLIT>
 __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
@@ -123,13 +125,22 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const int32_t wq_last = p + min((int32_t)n, iw0 + 32) - 1;
 
   // ---- buffer descriptors (byte offsets relative to this unit's first row)
-  const uint32_t q_row = H * DQK * 2, kv_row = H * DNOPE * 2;
-  const auto q_rs = rsrc(static_cast<const uint8_t*>(a.q) + ((size_t)t0 * H + h) * DQK * 2,
-                         (n - 1) * q_row + DQK * 2);
+  // (split Q: q_rs covers q_nope rows of 128 columns, qr_rs the q_rope rows)
+  constexpr uint32_t QW = QSPLIT ? DNOPE : DQK;       // columns of one row of the tensor at a.q
+  const uint32_t q_row = H * QW * 2, kv_row = H * DNOPE * 2;
+  const auto q_rs = rsrc(static_cast<const uint8_t*>(a.q) + ((size_t)t0 * H + h) * QW * 2, (n - 1) * q_row + QW * 2);
+  const uint32_t qr_row = H * (DQK - DNOPE) * 2;
+  const auto qr_rs = rsrc(QSPLIT ? static_cast<const uint8_t*>(a.q_rope) + ((size_t)t0 * H + h) * (DQK - DNOPE) * 2
+                                 : nullptr,
+                          QSPLIT ? (n - 1) * qr_row + (DQK - DNOPE) * 2 : 0u);
+  // contiguous K_rope (split Q only): key j of the sequence is row g0 + j, 128 bytes
+  const bool contig = QSPLIT && a.rope_rows != nullptr;
   const uint32_t kv_bytes = jend > 0 ? (uint32_t)(jend - 1) * kv_row + DNOPE * 2 : 0u;
   const auto kn_rs = rsrc(static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE * 2, kv_bytes);
   const auto v_rs = rsrc(static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE * 2, kv_bytes);
-  const auto cr_rs = rsrc(a.cache, a.cache_bytes);
+  const auto cr_rs = contig ? rsrc(static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * 128,
+                                    jend > 0 ? (uint32_t)jend * 128u : 0u)
+                           : rsrc(a.cache, a.cache_bytes);
   const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
   const uint32_t cache_row = a.row_width * 2;
 
@@ -139,8 +150,16 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   bf16x8 qop[12];
   auto load_q = [&]() {
     const uint32_t qoff = (uint32_t)my_i * q_row + hf * 16;
+    if constexpr (QSPLIT) {
+      const uint32_t qroff = (uint32_t)my_i * qr_row + hf * 16;
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, bload16(q_rs, qoff + ks * 32));
+      for (int ks = 0; ks < 8; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, bload16(q_rs, qoff + ks * 32));
+#pragma unroll
+      for (int ks = 8; ks < 12; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, bload16(qr_rs, qroff + (ks - 8) * 32));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, bload16(q_rs, qoff + ks * 32));
+    }
   };
 
   // ---- this lane's slots of a tile load (one 1 KiB load = 64 slots of 16 B)
@@ -163,6 +182,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     kr_chunk[u] = (lane & 7) ^ ((r >> 1) & 7);
   }
   auto page_of = [&](int32_t kt, int u) -> uint32_t {
+    if (contig) return 0u;
     const int32_t j = min(kt * BN + kr_row[u], jend - 1);   // clamped: always a valid position
     const uint32_t pos = (uint32_t)(c0 + j);
     return a.page_shift < 32u ? PT[pos >> a.page_shift] : PT[pos / a.page_size];
@@ -188,7 +208,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       const int32_t j = min(kt * BN + kr_row[u], jend - 1);
       const uint32_t pos = (uint32_t)(c0 + j);
       const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
-      const uint32_t off = (pg[u] * a.page_size + slot) * cache_row + a.rope_col * 2 + 16u * kr_chunk[u];
+      const uint32_t off = contig ? (uint32_t)j * 128u + 16u * kr_chunk[u]
+                                  : (pg[u] * a.page_size + slot) * cache_row + a.rope_col * 2 + 16u * kr_chunk[u];
       bload_lds(cr_rs, off, st + KR_OFF + m * 1024);
     }
   };
@@ -379,8 +400,11 @@ hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream
   const uint64_t grid = (units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   const bool plain = !a.out_fp32 && !a.lse && !a.prev_out && !a.row_mode;
-  auto kernel = a.causal ? (plain ? prefill_bf16_kernel<true, true> : prefill_bf16_kernel<true, false>)
-                         : (plain ? prefill_bf16_kernel<false, true> : prefill_bf16_kernel<false, false>);
+  auto kernel = a.q_split
+      ? (a.causal ? (plain ? prefill_bf16_kernel<true, true, true> : prefill_bf16_kernel<true, false, true>)
+                  : (plain ? prefill_bf16_kernel<false, true, true> : prefill_bf16_kernel<false, false, true>))
+      : (a.causal ? (plain ? prefill_bf16_kernel<true, true, false> : prefill_bf16_kernel<true, false, false>)
+                  : (plain ? prefill_bf16_kernel<false, true, false> : prefill_bf16_kernel<false, false, false>));
   hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }

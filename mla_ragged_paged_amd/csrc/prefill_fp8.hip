@@ -20,6 +20,8 @@
 //     V converted exactly from e4m3 to bf16 and bf16 p.
 //   * V is read transposed with ds_read_b64_tr_b8 (8 keys of one dv column per
 //     lane); s_v is applied to O in the epilogue.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -35,11 +37,12 @@ constexpr float RESCALE_LOG2 = 8.0f;
 // LDS stage layout (bytes): rows of fp8, 16-byte chunks XOR-swizzled per row
 constexpr int KN_OFF = 0;                      // K_nope [64 rows][8 chunks]
 constexpr int KR_OFF = KN_OFF + BN * 128;      // K_rope [64 rows][4 chunks]
-constexpr int V_OFF = KR_OFF + BN * 64;        // V      [64 rows][8 chunks]
-constexpr int STAGE = V_OFF + BN * 128;        // 20 KiB
+// V [64 rows][8 chunks] follows K_rope: at KR_OFF + 64 * 64 (20 KiB stages) when
+// K_rope is e4m3, at KR_OFF + 64 * 128 (24 KiB) when it is bf16 (the kernel's QM)
 
 __device__ __forceinline__ int swz_kn(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_kr(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_krb(int r) { return (r >> 1) & 7; }   // bf16 K_rope rows (8 chunks)
 __device__ __forceinline__ int swz_v(int r) { return 2 * (((r >> 1) & 1) | ((r >> 2) & 2)); }
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -71,9 +74,18 @@ __device__ __forceinline__ i32x2 e4m3x4_to_bf16x4(int x) {
 }  // namespace
 
 // CAUSAL: causal mask, else the null mask.  PLAIN: bf16 output only (no
-// log-sum-exp, no earlier partial to merge).
-template <bool CAUSAL, bool PLAIN>
+// log-sum-exp, no earlier partial to merge).  QM: how the query and K_rope come:
+//   0  q [T][H][192] e4m3 with q_scale; K_rope e4m3 from the paged cache;
+//   1  split: q_nope [T][H][128] e4m3 with q_scale and q_rope [T][H][64] bf16;
+//      K_rope e4m3 from the paged cache, converted exactly to bf16 for the rope
+//      product, which runs on the bf16 MFMA;
+//   2  split as 1, K_rope bf16 (paged bf16 cache or contiguous rows laid out like K).
+template <bool CAUSAL, bool PLAIN, int QM>
 __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
+  // K_rope rows of a stage: 64 bytes (e4m3) or 128 bytes (bf16)
+  constexpr int KR_ROW = QM == 2 ? 128 : 64;
+  constexpr int V_OFF = KR_OFF + BN * KR_ROW;
+  constexpr int STAGE = V_OFF + BN * 128;
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
 
@@ -117,29 +129,48 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   const int32_t wq_first = p + iw0;
   const int32_t wq_last = p + min((int32_t)n, iw0 + 32) - 1;
 
-  // per-tensor dequantisation scales
-  const float s_q = *a.q_scale, s_kn = *a.k_nope_scale, s_v = *a.v_scale, s_kr = *a.k_rope_scale;
+  // per-tensor dequantisation scales (a bf16 K_rope carries none)
+  const float s_q = *a.q_scale, s_kn = *a.k_nope_scale, s_v = *a.v_scale;
+  const float s_kr = QM == 2 ? 1.f : *a.k_rope_scale;
 
-  const uint32_t q_row = H * DQK, kv_row = H * DNOPE;
-  const auto q_rs = rsrc(static_cast<const uint8_t*>(a.q) + ((size_t)t0 * H + h) * DQK, (n - 1) * q_row + DQK);
+  constexpr uint32_t QW = QM == 0 ? DQK : DNOPE;      // e4m3 columns of one row of the tensor at a.q
+  const uint32_t q_row = H * QW, kv_row = H * DNOPE;
+  const auto q_rs = rsrc(static_cast<const uint8_t*>(a.q) + ((size_t)t0 * H + h) * QW, (n - 1) * q_row + QW);
+  const uint32_t qr_row = H * (DQK - DNOPE) * 2;       // bf16 q_rope (split query)
+  const auto qr_rs = rsrc(QM != 0 ? static_cast<const uint8_t*>(a.q_rope) + ((size_t)t0 * H + h) * (DQK - DNOPE) * 2
+                                  : nullptr,
+                          QM != 0 ? (n - 1) * qr_row + (DQK - DNOPE) * 2 : 0u);
+  // contiguous bf16 K_rope (QM 2 only): key j of the sequence is row g0 + j
+  const bool contig = QM == 2 && a.rope_rows != nullptr;
   const uint32_t kv_bytes = jend > 0 ? (uint32_t)(jend - 1) * kv_row + DNOPE : 0u;
   const auto kn_rs = rsrc(static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE, kv_bytes);
   const auto v_rs = rsrc(static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE, kv_bytes);
-  const auto cr_rs = rsrc(a.cache, a.cache_bytes);
+  const auto cr_rs = contig ? rsrc(static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * 128,
+                                    jend > 0 ? (uint32_t)jend * 128u : 0u)
+                           : rsrc(a.cache, a.cache_bytes);
   const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
-  const uint32_t cache_row = a.row_width;
+  const uint32_t cache_row = a.row_width * (QM == 2 ? 2u : 1u);   // bytes of one cache row
 
   // ---- Q^T operands: lane (li, hf) holds bytes [64ks + 32hf, +32) of its query.
   // Loaded after the first tile's page ids and K_nope / V loads (vector-memory
   // waits are in issue order); a negative scale's sign is applied once Q is in.
+  // Split query: qop[0..1] hold q_nope's bytes as above, and qr[r] holds q_rope
+  // columns [16r + 8hf, +8) in bf16 (the 32x32x16 bf16 MFMA's B operand).
+  constexpr int QKS = QM == 0 ? 3 : 2;                // e4m3 k-steps held in qop
   i32x8 qop[3];
+  bf16x8 qr[4];
   auto load_q = [&]() {
     const uint32_t qoff = (uint32_t)my_i * q_row + hf * 32;
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
+    for (int ks = 0; ks < QKS; ++ks) {
       const i32x4 x0 = bload16(q_rs, qoff + ks * 64);
       const i32x4 x1 = bload16(q_rs, qoff + ks * 64 + 16);
       qop[ks] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
+    if constexpr (QM != 0) {
+      const uint32_t qroff = (uint32_t)my_i * qr_row + hf * 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qr[r] = __builtin_bit_cast(bf16x8, bload16(qr_rs, qroff + r * 32));
     }
   };
 
@@ -152,10 +183,24 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
     kn_off[u] = (uint32_t)r * kv_row + 16u * (uint32_t)(cs ^ swz_kn(r));
     v_off[u] = (uint32_t)r * kv_row + 16u * (uint32_t)(cs ^ swz_v(r));
   }
-  const int kr_row = 16 * w + (lane >> 2);           // K_rope load m = w: rows 16m .. 16m+15
-  const int kr_chunk = (lane & 3) ^ swz_kr(kr_row);
-  auto page_of = [&](int32_t kt) -> uint32_t {
-    const int32_t j = min(kt * BN + kr_row, jend - 1);
+  // K_rope, e4m3 rows: load m = w covers rows 16m .. 16m+15, slot lane -> row
+  // 16m + lane/4.  bf16 rows (QM 2): loads m = 2w + u cover rows 8m .. 8m+7, slot
+  // lane -> row 8m + lane/8, chunk (lane % 8) ^ swz_krb(row).
+  constexpr int KRL = QM == 2 ? 2 : 1;               // K_rope loads per wave and tile
+  int kr_row[KRL], kr_chunk[KRL];
+#pragma unroll
+  for (int u = 0; u < KRL; ++u) {
+    if constexpr (QM == 2) {
+      kr_row[u] = 16 * w + 8 * u + (lane >> 3);
+      kr_chunk[u] = (lane & 7) ^ swz_krb(kr_row[u]);
+    } else {
+      kr_row[u] = 16 * w + (lane >> 2);
+      kr_chunk[u] = (lane & 3) ^ swz_kr(kr_row[u]);
+    }
+  }
+  auto page_of = [&](int32_t kt, int u) -> uint32_t {
+    if (contig) return 0u;
+    const int32_t j = min(kt * BN + kr_row[u], jend - 1);
     const uint32_t pos = (uint32_t)(c0 + j);
     return a.page_shift < 32u ? PT[pos >> a.page_shift] : PT[pos / a.page_size];
   };
@@ -172,12 +217,18 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       bload_lds(v_rs, jrow + v_off[u], st + V_OFF + m * 1024);
     }
   };
-  auto issue_rope = [&](int32_t kt, uint8_t* stage, uint32_t pg) {
+  auto issue_rope = [&](int32_t kt, uint8_t* stage, const uint32_t (&pg)[2]) {
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)stage;
-    const int32_t j = min(kt * BN + kr_row, jend - 1);
-    const uint32_t pos = (uint32_t)(c0 + j);
-    const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
-    bload_lds(cr_rs, (pg * a.page_size + slot) * cache_row + a.rope_col + 16u * kr_chunk, st + KR_OFF + w * 1024);
+#pragma unroll
+    for (int u = 0; u < KRL; ++u) {
+      const int32_t j = min(kt * BN + kr_row[u], jend - 1);
+      const uint32_t pos = (uint32_t)(c0 + j);
+      const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
+      const uint32_t el = QM == 2 ? 2u : 1u;
+      const uint32_t off = contig ? (uint32_t)j * 128u + 16u * kr_chunk[u]
+                                  : (pg[u] * a.page_size + slot) * cache_row + a.rope_col * el + 16u * kr_chunk[u];
+      bload_lds(cr_rs, off, st + KR_OFF + (KRL * w + u) * 1024);
+    }
   };
 
   // ---- LDS read offsets.  K operand (fp8 32x32x64): row R = 32kb + li, bytes
@@ -189,6 +240,14 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
     for (int x = 0; x < 2; ++x) kn_rd[ks][x] = KN_OFF + li * 128 + 16 * ((4 * ks + 2 * hf + x) ^ swz_kn(li));
 #pragma unroll
   for (int x = 0; x < 2; ++x) kr_rd[x] = KR_OFF + li * 64 + 16 * ((2 * hf + x) ^ swz_kr(li));
+  // split query, bf16 rope product (32x32x16): K operand row R = 32kb + li,
+  // columns [16r + 8hf, +8): e4m3 rows (QM 1) give 8 bytes at chunk r ^ swz_kr(R),
+  // half hf; bf16 rows (QM 2) 16 bytes at chunk (2r + hf) ^ swz_krb(R)
+  uint32_t krs_rd[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    krs_rd[r] = QM == 2 ? KR_OFF + li * 128 + 16 * ((2 * r + hf) ^ swz_krb(li))
+                        : KR_OFF + li * 64 + 16 * (r ^ swz_kr(li)) + 8 * hf;
   // V transposed byte reads (ds_read_b64_tr_b8: lane 16g + 2e + c supplies row e,
   // bytes 8c..8c+7; lane 16g + i receives column i of the 8 rows).  For 16-key
   // step t: rows 16t + 4(g>>1) + (e&3) + 8(e>>2), dv = 32d + 16(g&1) + 8c.
@@ -203,8 +262,11 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   }
 
   // ---- softmax state
-  const float c = a.scale_log2 * s_q * s_kr;         // exp2 factor for the combined score
-  const float ratio = s_kn / s_kr;                   // nope partial sum -> rope units
+  // exp2 factor for the combined score, and the factor taking the nope partial
+  // sum to the units of the rope one (q_scale applies to both halves of a full
+  // query, to q_nope only in a split one)
+  const float c = QM == 0 ? a.scale_log2 * s_q * s_kr : a.scale_log2 * s_kr;
+  const float ratio = QM == 0 ? s_kn / s_kr : s_q * s_kn / s_kr;
   const float thr = RESCALE_LOG2 / c;
   float m_run = -1e30f, mc = m_run * c, l_run = 0.f;
   f32x16 o[4];
@@ -213,10 +275,14 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
 
   // ---- prologue, ordered for the first tile's critical path: page ids first,
   // then the K_nope / V rows, then Q, so the K_rope loads wait for the page ids only
-  uint32_t pg_next = 0u;
+  uint32_t pg_next[2] = {0u, 0u};
   if (nkt > 0) {
-    const uint32_t pg0 = page_of(0);
-    pg_next = page_of(1);
+    uint32_t pg0[2] = {0u, 0u};
+#pragma unroll
+    for (int u = 0; u < KRL; ++u) {
+      pg0[u] = page_of(0, u);
+      pg_next[u] = page_of(1, u);
+    }
     // all four waves start their first tile together
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
@@ -234,19 +300,25 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
     __syncthreads();
     if (kt == 0 && a.scale < 0.f) {
 #pragma unroll
-      for (int ks = 0; ks < 3; ++ks) qop[ks] ^= (int)0x80808080;
+      for (int ks = 0; ks < QKS; ++ks) qop[ks] ^= (int)0x80808080;
+      if constexpr (QM != 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          qr[r] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(i32x4, qr[r]) ^ (int)0x80008000);
+      }
     }
     if (kt + 1 < nkt) {
       issue_kv(kt + 1, next);
       issue_rope(kt + 1, next, pg_next);
-      pg_next = page_of(kt + 2);
+#pragma unroll
+      for (int u = 0; u < KRL; ++u) pg_next[u] = page_of(kt + 2, u);
     }
     const int32_t j0 = kt * BN;
     if (!(wave_rows && (!causal || c0 + j0 <= wq_last))) return;
-    // S^T: two nope k-steps, scale to rope units, one rope k-step
+    // S^T: two nope k-steps, scale to rope units, the rope k-step(s)
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
+    for (int ks = 0; ks < QKS; ++ks) {
       i32x8 kf[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -262,6 +334,27 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_fp8(kf[kb], qop[ks], s[kb]);
+    }
+    if constexpr (QM != 0) {
+      // split query: nope sum to rope units, then four bf16 k-steps over the rope
+      // columns (e4m3 K_rope converted exactly to bf16 on the way)
+      s[0] *= ratio;
+      s[1] *= ratio;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          bf16x8 kfr;
+          if constexpr (QM == 2) {
+            kfr = *reinterpret_cast<const bf16x8*>(st + krs_rd[r] + kb * 32 * 128);
+          } else {
+            const i32x2 x = *reinterpret_cast<const i32x2*>(st + krs_rd[r] + kb * 32 * 64);
+            const i32x2 lo = e4m3x4_to_bf16x4(x[0]), hi = e4m3x4_to_bf16x4(x[1]);
+            kfr = __builtin_bit_cast(bf16x8, i32x4{lo[0], lo[1], hi[0], hi[1]});
+          }
+          s[kb] = mfma_bf16(kfr, qr[r], s[kb]);
+        }
+      }
     }
     const bool full = (j0 + BN <= len) && (!causal || c0 + j0 + BN - 1 <= wq_first);
     if (!full) {
@@ -379,8 +472,14 @@ hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream)
   const uint64_t grid = (units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   const bool plain = !a.out_fp32 && !a.lse && !a.prev_out && !a.row_mode;
-  auto kernel = a.causal ? (plain ? prefill_fp8_kernel<true, true> : prefill_fp8_kernel<true, false>)
-                         : (plain ? prefill_fp8_kernel<false, true> : prefill_fp8_kernel<false, false>);
+  auto pick = [&](auto qm) {
+    constexpr int QM = decltype(qm)::value;
+    return a.causal ? (plain ? prefill_fp8_kernel<true, true, QM> : prefill_fp8_kernel<true, false, QM>)
+                    : (plain ? prefill_fp8_kernel<false, true, QM> : prefill_fp8_kernel<false, false, QM>);
+  };
+  auto kernel = a.q_split == 0 ? pick(std::integral_constant<int, 0>{})
+                               : a.q_split == 1 ? pick(std::integral_constant<int, 1>{})
+                                                : pick(std::integral_constant<int, 2>{});
   hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }

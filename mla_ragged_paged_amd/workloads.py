@@ -173,6 +173,26 @@ def build(spec: Spec, n=None, p=None, page_permutation=None) -> Workload:
                     cache=cache, q=q, k_nope=kn, v=v, scales=scales)
 
 
+def split_query(w: Workload):
+    """The query as the two tensors of the split-Q calls: q_nope = columns 0..127
+    of w.q (bf16, or e4m3 codes that keep w.scales["q"]), q_rope [T, H, 64] bf16 =
+    columns 128..191 of w.q for a bf16 workload and, for an fp8 workload, a fresh
+    N(0, 1) draw rounded to bf16 (``torch.Generator().manual_seed(1000 + seed + 7919)``)."""
+    q_nope = w.q[..., :NOPE_DEPTH].contiguous()
+    if w.spec.dtype == "bf16":
+        return q_nope, w.q[..., NOPE_DEPTH:].contiguous()
+    gen = torch.Generator().manual_seed(1000 + w.spec.seed + 7919)
+    q_rope = torch.randn((w.total_q, w.heads, ROPE_DEPTH), generator=gen, dtype=torch.float32)
+    return q_nope, q_rope.to(torch.bfloat16)
+
+
+def draw_rope_rows(rows: int, seed: int) -> torch.Tensor:
+    """Contiguous K_rope rows [rows, 1, 64], N(0, 1) rounded to bf16
+    (``torch.Generator().manual_seed(1000 + seed + 104729)``)."""
+    gen = torch.Generator().manual_seed(1000 + seed + 104729)
+    return torch.randn((rows, 1, ROPE_DEPTH), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
 def causal_pairs(n, p) -> int:
     """Visible (query, key) pairs: every new token sees its prefix and itself."""
     n = np.asarray(n, dtype=np.int64)

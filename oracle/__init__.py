@@ -23,6 +23,7 @@ from .mla_oracle import (  # noqa: F401
     mla_prefill_ragged,
     mla_prefill_rows,
     mla_prefill_ragged_split,
+    mla_prefill_rows_split,
     merge_partials,
     MASKS,
 )

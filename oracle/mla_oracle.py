@@ -43,6 +43,7 @@ __all__ = [
     "mla_prefill_ragged",
     "mla_prefill_rows",
     "mla_prefill_ragged_split",
+    "mla_prefill_rows_split",
     "merge_partials",
 ]
 
@@ -469,4 +470,37 @@ def mla_prefill_ragged_split(q_nope, q_rope, k_nope, v, cache_lengths, valid_len
             vv = _as_f64(v[g0:g0 + count, h, :], sc.get("v") if fp8 else None)
             out[t0:t1, h, :], lse[t0:t1, h] = _attend(q[t0:t1, h, :], kn, kr, vv, scale, qpos, kpos, mask)
     return (out, lse) if return_lse else out
+
+
+def mla_prefill_rows_split(rows, q_nope, q_rope, k_nope, v, cache_lengths, valid_length, cache_row_offsets,
+                           cache_offsets, scale, k_rope_rows=None, cache=None, layer_idx=0, page_table=None,
+                           page_size=None, rope_col=None, scales=None, mask="causal"):
+    """Selected (t, h) outputs of ``mla_prefill_ragged_split``, float64 [len(rows), 128],
+    evaluated one output row at a time (for large problems)."""
+    sc = scales or {}
+    fp8 = scales is not None
+    vl = np.asarray(valid_length, dtype=np.int64)
+    cro = np.asarray(cache_row_offsets, dtype=np.int64)
+    co = None if cache_offsets is None else np.asarray(cache_offsets, dtype=np.int64)
+    p = np.asarray(cache_lengths, dtype=np.int64)
+    B = vl.shape[0] - 1
+    out = np.zeros((len(rows), NOPE_DEPTH), dtype=np.float64)
+    for idx, (t, h) in enumerate(rows):
+        b = int(np.searchsorted(vl, t, side="right") - 1)
+        assert 0 <= b < B and vl[b] <= t < vl[b + 1]
+        i = t - vl[b]
+        g0, count = _sequence_keys(b, cro)
+        kpos = _key_positions(co, b, count)
+        qpos = _query_positions(p, b, i + 1)[i:i + 1]
+        qrow = np.concatenate([_as_f64(q_nope[t:t + 1, h, :], sc.get("q") if fp8 else None),
+                               _as_f64(q_rope[t:t + 1, h, :])], axis=1)
+        kn = _as_f64(k_nope[g0:g0 + count, h, :], sc.get("k_nope") if fp8 else None)
+        vv = _as_f64(v[g0:g0 + count, h, :], sc.get("v") if fp8 else None)
+        if k_rope_rows is not None:
+            kr = _as_f64(k_rope_rows[g0:g0 + count]).reshape(count, ROPE_DEPTH)
+        else:
+            kr = _as_f64(rope_rows(cache, layer_idx, page_table, page_size, rope_col, b, kpos),
+                         sc.get("k_rope") if fp8 else None)
+        out[idx] = _attend(qrow, kn, kr, vv, scale, qpos, kpos, mask)[0][0]
+    return out
 

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_merge",
                                     "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_lse",
-                                    "mla_prefill_ragged_row", "mla_status_string"]
+                                    "mla_prefill_ragged_row", "mla_prefill_ragged_split", "mla_status_string"]
 
 
 def test_binding_exposes_every_entry_point():
@@ -121,6 +121,19 @@ def test_lse_and_merge_validation_without_gpu():
     assert lib.mla_prefill_ragged_row(*row_args(acc=None)) == 1
     assert lib.mla_prefill_ragged_row(*row_args(acc_lse=None)) == 1
     assert lib.mla_prefill_ragged_row(*row_args(acc=ctypes.c_void_p(24))) == 2    # misaligned accumulator
+
+    def split_args(**kw):
+        return [dummy, 0, None, dummy, kw.get("qr", dummy), kw.get("dt", 0), kw.get("qs"), dummy, kw.get("ks"),
+                dummy, kw.get("vs"), kw.get("rows", dummy), ref, 0, dummy, dummy, None, 1, 4, 2, kw.get("d", 128),
+                0, ctypes.c_float(0.07), 0, None]
+    assert lib.mla_prefill_ragged_split(*split_args(qr=None)) == 1            # q_rope missing
+    assert lib.mla_prefill_ragged_split(*split_args(dt=1)) == 1               # fp8 without scales
+    assert lib.mla_prefill_ragged_split(*split_args(qs=dummy)) == 3           # scales given for bf16
+    assert lib.mla_prefill_ragged_split(*split_args(d=64)) == 4
+    assert lib.mla_prefill_ragged_split(*split_args(rows=ctypes.c_void_p(24))) == 2   # misaligned rope rows
+    s.dtype = 1
+    assert lib.mla_prefill_ragged_split(*split_args(rows=None)) == 3          # bf16 q_nope with an e4m3 cache
+    s.dtype = 0
 
     def merge_args(**kw):
         return [kw.get("out", dummy), kw.get("odt", 0), kw.get("lse"), kw.get("oa", dummy), dummy, dummy,

@@ -150,3 +150,30 @@ def test_contiguous_rope_is_indexed_by_buffer_row():
                  cache_row_offsets=np.array([gap, bro[1] + gap, bro[2] + gap], dtype=np.uint32))
     b = _split(common, moved, k_rope_rows=kr[idx], cache=None)
     assert np.array_equal(a, b)
+
+
+def test_sampled_split_rows_match_full_output():
+    rng = np.random.default_rng(714)
+    common, rows, meta = make_problem(rng, [5, 0, 7], [1, 2, 3], heads=2, cap=6)
+    qn_c, sq = _q8(common["q"][..., :128])
+    qr = common["q"][..., 128:]
+    cache_c, skr = _q8(common["cache"])
+    picks = [(0, 1), (4, 0), (5, 1), (11, 0)]
+    for row in rows:
+        kn_c, skn = _q8(row["k_nope"])
+        v_c, sv = _q8(row["v"])
+        scales = {"q": sq, "k_nope": skn, "v": sv, "k_rope": skr}
+        for contig in (False, True):
+            kw = dict(q_nope=qn_c, q_rope=qr, k_nope=kn_c, v=v_c, scales=scales, mask="null" if contig else "causal")
+            if contig:
+                kw["k_rope_rows"] = _contiguous_rope(common, row, meta)
+            else:
+                kw["cache"] = cache_c
+            full = _split(common, row, **kw)
+            got = oracle.mla_prefill_rows_split(
+                picks, qn_c, qr, kn_c, v_c, common["cache_lengths"], common["valid_length"],
+                row["cache_row_offsets"], row["cache_offsets"], common["scale"], k_rope_rows=kw.get("k_rope_rows"),
+                cache=kw.get("cache"), page_table=common["page_table"], page_size=common["page_size"],
+                rope_col=common["rope_col"], scales=scales, mask=kw["mask"])
+            for k, (t, h) in enumerate(picks):
+                assert np.abs(got[k] - full[t, h]).max() <= 1e-13
