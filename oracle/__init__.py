@@ -24,6 +24,7 @@ from .mla_oracle import (  # noqa: F401
     mla_prefill_rows,
     mla_prefill_ragged_split,
     mla_prefill_rows_split,
+    latent_up,
     merge_partials,
     MASKS,
 )

@@ -44,6 +44,7 @@ __all__ = [
     "mla_prefill_rows",
     "mla_prefill_ragged_split",
     "mla_prefill_rows_split",
+    "latent_up",
     "merge_partials",
 ]
 
@@ -503,4 +504,30 @@ def mla_prefill_rows_split(rows, q_nope, q_rope, k_nope, v, cache_lengths, valid
                          sc.get("k_rope") if fp8 else None)
         out[idx] = _attend(qrow, kn, kr, vv, scale, qpos, kpos, mask)[0][0]
     return out
+
+
+def latent_up(cache, layer_idx, page_table, page_size, buffer_row_offsets_r, cache_offsets_r, latent_col,
+              latent_dim, w_kv, heads, cap):
+    """Per-head K_nope and V of one buffer row from the latent cache, float64.
+
+    The pages call the cache a latent cache ("mla_prefill_v2_ragged", Args: the
+    V operand is the nope segment of the latent cache) and give no
+    decompression step; reading R-y takes the DeepSeek-V2/V3 form: each cache
+    row holds a latent vector c (columns latent_col .. latent_col+latent_dim-1)
+    and the per-head keys and values are linear in it,
+      K_nope[g][h][d] = sum_c w_kv[h*256 + d][c]       * c_g[c]
+      V[g][h][d]      = sum_c w_kv[h*256 + 128 + d][c] * c_g[c]
+    with w_kv [heads*256][latent_dim] (per head, 128 key rows then 128 value
+    rows) and c_g the latent of the cache position that buffer slot g holds
+    under the plan row (``gather``).  Returns (k_nope, v), each [cap, heads,
+    128]; slots the row does not use are 0.
+    """
+    lat = gather(cache, layer_idx, page_table, page_size, buffer_row_offsets_r, cache_offsets_r,
+                 latent_col, latent_dim, np.zeros((cap, latent_dim)))
+    lat = np.asarray(lat, dtype=np.float64)
+    used = int(np.asarray(_host_array(buffer_row_offsets_r), dtype=np.int64)[-1])
+    lat[used:] = 0.0
+    w = _as_f64(w_kv).reshape(heads, 2, NOPE_DEPTH, latent_dim)
+    kv = np.einsum("gc,hpdc->gphd", lat, w)            # [cap, 2, heads, 128]
+    return kv[:, 0], kv[:, 1]
 

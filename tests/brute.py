@@ -89,3 +89,28 @@ def attention_brute(q, k_nope, v, rope, cache_lengths, valid_length, cache_row_o
                 out[t][h] = [a / wsum for a in acc]
                 lse[t][h] = top + math.log(wsum)
     return (out, lse) if with_lse else out
+
+
+def latent_up_brute(cache_rows, bro, co, w, heads, cap, latent_dim):
+    """K_nope / V of each buffer slot by explicit loops.
+
+    cache_rows(b, pos) -> list of latent_dim floats (the latent of that cache
+    position); bro / co one plan row; w[n][c] nested lists, n = h*256 + part*128 + d.
+    Returns (k, v) as nested lists [cap][heads][128]; unused slots are 0.
+    """
+    k = [[[0.0] * 128 for _ in range(heads)] for _ in range(cap)]
+    v = [[[0.0] * 128 for _ in range(heads)] for _ in range(cap)]
+    for b in range(len(co)):
+        for j in range(bro[b + 1] - bro[b]):
+            g = bro[b] + j
+            lat = cache_rows(b, co[b] + j)
+            for h in range(heads):
+                for d in range(128):
+                    sk = 0.0
+                    sv = 0.0
+                    for c in range(latent_dim):
+                        sk += w[h * 256 + d][c] * lat[c]
+                        sv += w[h * 256 + 128 + d][c] * lat[c]
+                    k[g][h][d] = sk
+                    v[g][h][d] = sv
+    return k, v

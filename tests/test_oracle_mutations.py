@@ -10,6 +10,7 @@ from tests import test_oracle_attention as A
 from tests import test_oracle_fp8 as F
 from tests import test_oracle_masks_merge as M
 from tests import test_oracle_split as S
+from tests import test_oracle_latent as L
 
 
 def _pins():
@@ -32,6 +33,9 @@ def _pins():
     pins += [lambda m=m: S.test_halves_of_one_query_equal_that_query(m) for m in ("causal", "null")]
     pins += [S.test_q_scale_scales_q_nope_only, S.test_contiguous_rope_equals_paged_rope,
              S.test_contiguous_rope_is_indexed_by_buffer_row]
+    pins += [lambda c=c: L.test_latent_up_matches_brute_force(c) for c in range(len(L.CASES))]
+    pins += [L.test_one_hot_weights_select_latent_columns, L.test_linear_in_the_weights_and_halves_in_place,
+             L.test_unused_slots_are_zero_and_rows_follow_the_plan]
     return pins
 
 
@@ -50,6 +54,7 @@ _orig_visible = om._visible
 _orig_rope = om.rope_rows
 _orig_merge = om.merge_partials
 _orig_split = om.mla_prefill_ragged_split
+_orig_latent = om.latent_up
 
 
 def _attend_no_rope(q, kn, kr, v, scale, qpos, kpos, mask="causal"):
@@ -146,6 +151,25 @@ def _split_k_rope_scale_dropped(*args, scales=None, **kw):
     return _orig_split(*args, scales=scales, **kw)
 
 
+def _latent_halves_swapped(*args):
+    k, v = _orig_latent(*args)
+    return v, k
+
+
+def _latent_head_major_misread(cache, layer_idx, pt, ps, bro, co, latent_col, latent_dim, w, heads, cap):
+    w = np.asarray(w).reshape(2, heads, 128, latent_dim).transpose(1, 0, 2, 3).reshape(heads * 256, latent_dim)
+    return _orig_latent(cache, layer_idx, pt, ps, bro, co, latent_col, latent_dim, w, heads, cap)
+
+
+def _latent_column_off_by_one(cache, layer_idx, pt, ps, bro, co, latent_col, latent_dim, w, heads, cap):
+    return _orig_latent(cache, layer_idx, pt, ps, bro, co, latent_col + 1, latent_dim, w, heads, cap)
+
+
+def _latent_offsets_ignored(cache, layer_idx, pt, ps, bro, co, latent_col, latent_dim, w, heads, cap):
+    return _orig_latent(cache, layer_idx, pt, ps, bro, np.zeros_like(np.asarray(co)), latent_col, latent_dim, w,
+                        heads, cap)
+
+
 def _rope_logical_pages(cache, layer_idx, page_table, page_size, rope_col, b, positions):
     pt = np.asarray(om._host_array(page_table)).copy()
     pt[b] = np.arange(pt.shape[1])
@@ -183,6 +207,10 @@ MUTATIONS = {
     "split: q_rope ignored": ("mla_prefill_ragged_split", _split_rope_ignored),
     "split: contiguous rope indexed by position": ("mla_prefill_ragged_split", _split_contig_by_position),
     "split: cache scale of K_rope dropped": ("mla_prefill_ragged_split", _split_k_rope_scale_dropped),
+    "latent: key and value halves swapped": ("latent_up", _latent_halves_swapped),
+    "latent: weight rows read part-major": ("latent_up", _latent_head_major_misread),
+    "latent: columns off by one": ("latent_up", _latent_column_off_by_one),
+    "latent: plan cache offsets ignored": ("latent_up", _latent_offsets_ignored),
     "mask ignores the prefix": ("_query_positions", lambda p, b, count: np.arange(count, dtype=np.int64)),
     "cache_offsets ignored": ("_key_positions", lambda co, b, count: np.arange(count, dtype=np.int64)),
     "page table ignored": ("rope_rows", _rope_logical_pages),
