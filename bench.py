@@ -167,7 +167,8 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
     """The paths beside the headline step, on the same workload:
     the null mask (every key visible), the context cut into three buffer rows
     whose partials merge in the attention epilogue, the split-query calls (also
-    on the fp8 workload), and the standalone merge kernel's bandwidth on fp32
+    on the fp8 workload), the latent decompression (and the step that uses it
+    instead of the gather), and the standalone merge kernel's bandwidth on fp32
     partials."""
     from mla_ragged_paged_amd import _binding as B
     from mla_ragged_paged_amd import workloads
@@ -230,6 +231,22 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
                 "achieved_TFLOPs": round(fl / (med * 1e-3) / 1e12, 2),
                 "frac_of_peak": round(fl / (med * 1e-3) / 1e12 / pk, 4)}
         del st
+
+    # latent decompression (K_nope / V from the latent cache, synthetic weights)
+    # and the step that uses it in place of the gather
+    if w.spec.dtype == "bf16":
+        Wkv = workloads.draw_kv_b_weight(w.heads, 512, seed=w.spec.seed)
+        ls = PrefillStep(w, "cuda:0", kv_b_weight=Wkv)
+        ls.run()
+        med_up, best_up = _median_ms(torch, lambda: ls.latent_up(0), reps, stream)
+        med_step, _ = _median_ms(torch, ls.run, reps, stream)
+        fl_up = 2.0 * w.total_ctx * 512 * w.heads * 256
+        out["latent_up"] = {"slots": w.total_ctx, "latent_dim": 512, "heads": w.heads, "tflop": round(fl_up / 1e12, 5),
+                            "median_ms": round(med_up, 4), "min_ms": round(best_up, 4),
+                            "achieved_TFLOPs": round(fl_up / (med_up * 1e-3) / 1e12, 2),
+                            "frac_of_peak": round(fl_up / (med_up * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                            "latent_step_median_ms": round(med_step, 4)}
+        del ls
 
     T, H = 16384, 128
     dev = torch.device("cuda:0")

@@ -19,6 +19,9 @@
  *                       contiguous rows (page "flare_mla_prefill", the q_nope /
  *                       q_rope / q_scale / k_scales overloads).
  *
+ *   mla_prefill_latent_up  per-head K_nope / V of one buffer row, up-projected
+ *                       from the latent part of the cache rows the plan row holds.
+ *
  * When the plan cuts the contexts over several buffer rows, each row's
  * attention covers part of a sequence's keys:
  *
@@ -172,6 +175,40 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
                                 const uint32_t* buffer_row_offsets_r, const uint32_t* cache_offsets_r,
                                 uint32_t col_begin, uint32_t col_count, uint32_t buffer_token_size,
                                 void* out, void* stream);
+
+/*
+ * mla_prefill_latent_up -- the K_nope / V buffer of one plan row, decompressed
+ * from the latent cache.  The pages describe the cache as a latent cache (page
+ * "mla_prefill_v2_ragged", Args: V is the nope segment of the latent cache)
+ * and the plan that says which cache positions fill which buffer slots (page
+ * "generic_flare_mla_prefill_ragged_paged_plan"); the decompression is the
+ * DeepSeek-V2/V3 one.  For every b < batch_size, j < bro[b+1] - bro[b], slot
+ * g = bro[b] + j and head h:
+ *   c_g              = cache row of sequence b at position co[b] + j, columns
+ *                      latent_col .. latent_col + latent_dim - 1 (as mla_prefill_gather)
+ *   k_nope[g][h][d]  = sum_c w_kv[h*256 + d][c]       * c_g[c]     (d < 128)
+ *   v[g][h][d]       = sum_c w_kv[h*256 + 128 + d][c] * c_g[c]
+ * accumulated in fp32 and rounded to bf16 (nearest-even).  Slots at or beyond
+ * bro[batch_size] are not written.
+ *
+ *   kv                   [host] bf16 cache descriptor (page table, rows).
+ *   buffer_row_offsets_r, cache_offsets_r  one plan row, as for mla_prefill_gather.
+ *   latent_col, latent_dim  latent column window; latent_dim a positive multiple
+ *                        of 64, latent_col * 2 bytes a multiple of 16.
+ *   w_kv                 device bf16 [num_heads * 256][latent_dim]: per head 128
+ *                        key rows then 128 value rows (a linear layer's weight,
+ *                        output features by input features).
+ *   buffer_token_size    slots of k_nope / v (the plan's cap).
+ *   k_nope, v            device bf16 [buffer_token_size][num_heads][128] (outputs),
+ *                        16-byte aligned.
+ * Errors: NULL_ARG, UNSUPPORTED_DTYPE (cache not bf16), BAD_SHAPE (window,
+ * alignment, batch_size > MLA_MAX_BATCH, sizes past 32-bit offsets), HIP.
+ */
+mla_status_t mla_prefill_latent_up(const mla_paged_cache_t* kv, uint32_t layer_idx, uint32_t batch_size,
+                                   const uint32_t* buffer_row_offsets_r, const uint32_t* cache_offsets_r,
+                                   uint32_t latent_col, uint32_t latent_dim, const void* w_kv,
+                                   uint32_t num_heads, uint32_t buffer_token_size, void* k_nope, void* v,
+                                   void* stream);
 
 /*
  * mla_prefill_ragged -- page "flare_mla_prefill" (description, Args) with the

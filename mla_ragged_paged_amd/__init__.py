@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     mla_prefill_gather,
     mla_prefill_last_hip_error,
     mla_prefill_plan,
+    mla_prefill_latent_up,
     mla_prefill_merge,
     mla_prefill_ragged,
     mla_prefill_ragged_lse,

@@ -52,7 +52,7 @@ def library_path() -> str:
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m mla_ragged_paged_amd.build` "
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python mla_ragged_paged_amd/build.py` "
                           "(there is no non-HIP fallback)")
     lib = ctypes.CDLL(_LIB_PATH)
     u32, vp, i32 = ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
@@ -73,6 +73,8 @@ def _load():
     lib.mla_prefill_ragged_split.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, cp, u32, vp, vp, vp,
                                              u32, u32, u32, u32, i32, ctypes.c_float, u32, vp]
     lib.mla_prefill_ragged_split.restype = i32
+    lib.mla_prefill_latent_up.argtypes = [cp, u32, u32, vp, vp, u32, u32, vp, u32, u32, vp, vp, vp]
+    lib.mla_prefill_latent_up.restype = i32
     lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
     lib.mla_prefill_merge.restype = i32
     lib.mla_status_string.argtypes = [i32]
@@ -292,6 +294,23 @@ def mla_prefill_ragged_split(output, q_nope, q_rope, k_nope, v, kv: PagedCache, 
                                          k_nope.shape[2], _mask_code(mask), float(scale), int(q_max_seq_len),
                                          _stream(stream)),
            "mla_prefill_ragged_split")
+
+
+def mla_prefill_latent_up(kv: PagedCache, layer_idx, buffer_row_offsets_r, cache_offsets_r, w_kv, k_nope, v,
+                          latent_col=0, latent_dim=512, stream=None):
+    """K_nope / V [cap, H, 128] of one plan row from the latent cache and w_kv [H*256, latent_dim] (bf16)."""
+    cap, H, d = k_nope.shape
+    _contiguous(w_kv=w_kv, k_nope=k_nope, v=v)
+    if d != 128 or tuple(v.shape) != (cap, H, 128):
+        raise ValueError("k_nope and v must be [cap, H, 128]")
+    if tuple(w_kv.shape) != (H * 256, latent_dim) or w_kv.dtype != torch.bfloat16:
+        raise ValueError(f"w_kv must be bf16 of shape {(H * 256, latent_dim)}")
+    batch = cache_offsets_r.shape[0]
+    s = kv.as_struct()
+    _check(_lib.mla_prefill_latent_up(ctypes.byref(s), layer_idx, batch, _idx(buffer_row_offsets_r, "bro"),
+                                      _idx(cache_offsets_r, "cache_offsets"), latent_col, latent_dim, _ptr(w_kv), H,
+                                      cap, _ptr(k_nope), _ptr(v), _stream(stream)),
+           "mla_prefill_latent_up")
 
 
 def mla_prefill_merge(output, lse, o_a, lse_a, o_b, lse_b, stream=None):

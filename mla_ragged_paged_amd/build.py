@@ -1,6 +1,7 @@
 """Compile the HIP sources of the library into ``libmla_prefill.so`` (gfx950 only).
 
-Run as ``python -m mla_ragged_paged_amd.build``.  hipcc cross-compiles, so no GPU is
+Run as ``python mla_ragged_paged_amd/build.py`` (by path: importing the package
+loads the library, which a first build does not have yet).  hipcc cross-compiles, so no GPU is
 needed.  Packed fp32 VALU instructions are disabled for every kernel.
 """
 from __future__ import annotations
@@ -14,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_prefill.so")
-SOURCES = ["api.hip", "plan_gather.hip", "prefill_bf16.hip", "prefill_fp8.hip", "merge.hip"]
+SOURCES = ["api.hip", "plan_gather.hip", "prefill_bf16.hip", "prefill_fp8.hip", "merge.hip", "latent_up.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -297,6 +297,46 @@ mla_status_t mla_prefill_ragged_split(void* output, mla_dtype_t output_dtype, fl
                       depth, mask, scale, q_scale, k_scales, v_scale, q_max_seq_len, stream);
 }
 
+mla_status_t mla_prefill_latent_up(const mla_paged_cache_t* kv, uint32_t layer_idx, uint32_t batch_size,
+                                   const uint32_t* buffer_row_offsets_r, const uint32_t* cache_offsets_r,
+                                   uint32_t latent_col, uint32_t latent_dim, const void* w_kv, uint32_t num_heads,
+                                   uint32_t buffer_token_size, void* k_nope, void* v, void* stream) {
+  mla_status_t st = check_cache(kv, layer_idx);
+  if (st != MLA_OK) return st;
+  if (!buffer_row_offsets_r || !cache_offsets_r || !w_kv || !k_nope || !v) return MLA_ERR_NULL_ARG;
+  if (kv->dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED_DTYPE;
+  if (batch_size == 0 || num_heads == 0) return MLA_OK;
+  if (batch_size > MLA_MAX_BATCH || buffer_token_size == 0 || latent_dim == 0 || latent_dim % 64 ||
+      (uint64_t)latent_col + latent_dim > kv->row_width || (latent_col * 2) % 16 || (kv->row_width * 2) % 16)
+    return MLA_ERR_BAD_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(kv->data) | reinterpret_cast<uintptr_t>(w_kv) |
+       reinterpret_cast<uintptr_t>(k_nope) | reinterpret_cast<uintptr_t>(v)) % 16)
+    return MLA_ERR_BAD_SHAPE;
+  const uint64_t layer_bytes = (uint64_t)kv->num_pages * kv->page_size * kv->row_width * 2;
+  const uint64_t grid = ((uint64_t)buffer_token_size + 127) / 128 * 2 * num_heads;
+  if (layer_bytes >= (1ull << 32) || 128ull * latent_dim * 2 >= (1ull << 31) || grid >= (1ull << 31))
+    return MLA_ERR_BAD_SHAPE;
+  mla::LatentArgs a{};
+  a.cache = layer_base(kv, layer_idx);
+  a.page_table = kv->page_table;
+  a.bro = buffer_row_offsets_r;
+  a.co = cache_offsets_r;
+  a.w = static_cast<const uint16_t*>(w_kv);
+  a.k_nope = static_cast<uint16_t*>(k_nope);
+  a.v = static_cast<uint16_t*>(v);
+  a.max_pages = kv->max_pages_per_seq;
+  a.page_size = kv->page_size;
+  a.page_shift = (kv->page_size & (kv->page_size - 1)) == 0 ? (uint32_t)__builtin_ctz(kv->page_size) : 0xFFFFFFFFu;
+  a.row_bytes = kv->row_width * 2;
+  a.latent_col = latent_col;
+  a.latent_dim = latent_dim;
+  a.cache_bytes = (uint32_t)layer_bytes;
+  a.batch = batch_size;
+  a.heads = num_heads;
+  a.cap = buffer_token_size;
+  return hip_status(mla::launch_latent_up(a, static_cast<hipStream_t>(stream)));
+}
+
 mla_status_t mla_prefill_merge(void* output, mla_dtype_t output_dtype, float* lse, const float* o_a,
                                const float* lse_a, const float* o_b, const float* lse_b, uint32_t total_q_tokens,
                                uint32_t num_heads, uint32_t depth, void* stream) {

@@ -84,10 +84,31 @@ struct MergeArgs {
   uint32_t out_fp32;
 };
 
+struct LatentArgs {
+  const uint8_t* cache;               // layer base, [pages][page_size][1][row_width] bf16
+  const uint32_t* page_table;         // [B][max_pages]
+  const uint32_t* bro;                // [B+1] one plan row's buffer_row_offsets
+  const uint32_t* co;                 // [B]   its cache_offsets
+  const uint16_t* w;                  // [H*256][latent_dim] bf16
+  uint16_t* k_nope;                   // [cap][H][128] bf16
+  uint16_t* v;                        // [cap][H][128] bf16
+  uint32_t max_pages;
+  uint32_t page_size;
+  uint32_t page_shift;                // log2(page_size) when a power of two, else 0xFFFFFFFF
+  uint32_t row_bytes;                 // bytes of one cache row
+  uint32_t latent_col;                // first latent column of a cache row
+  uint32_t latent_dim;                // latent columns (a multiple of 64)
+  uint32_t cache_bytes;               // bytes of one layer (< 4 GiB)
+  uint32_t batch;
+  uint32_t heads;
+  uint32_t cap;                       // slots of K_nope / V
+};
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int unit, hipStream_t stream);
 hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream);
 hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_latent_up(const LatentArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -28,10 +28,14 @@ class PrefillStep:
 
     ``cap`` is the buffer-row capacity handed to the plan (default: the whole
     batch's context, one row).  ``gather_cols`` = (col_begin, col_count) of the
-    cache rows the gather copies (default: the whole row).
+    cache rows the gather copies (default: the whole row).  With ``kv_b_weight``
+    ([H*256, latent_dim] bf16) K_nope / V are not the workload's tensors but are
+    decompressed per buffer row from the latent cache (columns
+    ``latent_col`` .. +latent_dim), which replaces the gather step.
     """
 
-    def __init__(self, w: Workload, device="cuda", cap: int | None = None, gather_cols=None, mask="causal"):
+    def __init__(self, w: Workload, device="cuda", cap: int | None = None, gather_cols=None, mask="causal",
+                 kv_b_weight=None, latent_col=0):
         self.w = w
         self.mask = mask
         self.device = torch.device(device)
@@ -62,6 +66,11 @@ class PrefillStep:
         self.gather_cols = (0, width) if gather_cols is None else tuple(gather_cols)
         self.gathered = torch.zeros((self.cap, self.gather_cols[1]), dtype=w.cache.dtype, device=dev)
         self.out = torch.zeros((w.total_q, w.heads, 128), dtype=torch.bfloat16, device=dev)
+        self.kv_b_weight = None if kv_b_weight is None else kv_b_weight.to(dev).contiguous()
+        self.latent_col = latent_col
+        if self.kv_b_weight is not None:
+            self.kn_buf = torch.zeros((self.cap, w.heads, 128), dtype=torch.bfloat16, device=dev)
+            self.v_buf = torch.zeros((self.cap, w.heads, 128), dtype=torch.bfloat16, device=dev)
         # fp32 partial and log-sum-exp carried between buffer rows
         self.acc = None
         self.lse = None
@@ -74,6 +83,8 @@ class PrefillStep:
         sequence's context end to end in batch order (the one-row layout), and
         row r covers positions [r * cap, r * cap + buffer_lengths[r]) of that
         stream, so a row's buffer is a view at offset r * cap."""
+        if self.kv_b_weight is not None:
+            return self.kn_buf, self.v_buf
         lo = row * self.cap
         return self.k_nope[lo:], self.v[lo:]
 
@@ -84,6 +95,12 @@ class PrefillStep:
     def gather(self, row: int = 0, stream=None):
         B.mla_prefill_gather(self.kv, self.w.spec.layer_idx, self.buffer_row_offsets[row], self.cache_offsets[row],
                              self.gather_cols[0], self.gather_cols[1], self.gathered, stream)
+
+    def latent_up(self, row: int = 0, stream=None):
+        """K_nope / V of plan row ``row`` from the latent cache into the row buffers."""
+        B.mla_prefill_latent_up(self.kv, self.w.spec.layer_idx, self.buffer_row_offsets[row], self.cache_offsets[row],
+                                self.kv_b_weight, self.kn_buf, self.v_buf, latent_col=self.latent_col,
+                                latent_dim=self.kv_b_weight.shape[1], stream=stream)
 
     def attention(self, row: int = 0, k_nope=None, v=None, out=None, cache_offsets="plan", stream=None):
         """Attention over plan row ``row``; k_nope / v default to the workload's buffer (one-row layout)."""
@@ -106,13 +123,17 @@ class PrefillStep:
                                  v_scale=sc.get("v"), q_max_seq_len=self.w.max_q, stream=stream, mask=self.mask)
 
     def run(self, stream=None):
-        """The whole step: plan, then per buffer row its gather and its attention
-        (merged across rows when there are several)."""
+        """The whole step: plan, then per buffer row its gather (or its latent
+        decompression) and its attention (merged across rows when there are several)."""
         self.plan(stream)
-        if self.rows == 1:
-            self.gather(0, stream)
-            self.attention(0, stream=stream)
-            return
+        latent = self.kv_b_weight is not None
         for r in range(self.rows):
-            self.gather(r, stream)
-            self.attention_row_merged(r, stream)
+            if latent:
+                self.latent_up(r, stream)
+            else:
+                self.gather(r, stream)
+            if self.rows == 1:
+                kn, v = self.row_buffers(0)
+                self.attention(0, k_nope=kn, v=v, stream=stream)
+            else:
+                self.attention_row_merged(r, stream)

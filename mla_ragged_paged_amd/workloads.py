@@ -193,6 +193,16 @@ def draw_rope_rows(rows: int, seed: int) -> torch.Tensor:
     return torch.randn((rows, 1, ROPE_DEPTH), generator=gen, dtype=torch.float32).to(torch.bfloat16)
 
 
+def draw_kv_b_weight(heads: int, latent_dim: int, seed: int) -> torch.Tensor:
+    """Synthetic up-projection weight [heads * 256, latent_dim] bf16 (per head 128
+    key rows then 128 value rows), N(0, 1 / latent_dim) so that K_nope and V of an
+    N(0, 1) latent are about N(0, 1)
+    (``torch.Generator().manual_seed(1000 + seed + 15485863)``)."""
+    gen = torch.Generator().manual_seed(1000 + seed + 15485863)
+    w = torch.randn((heads * 256, latent_dim), generator=gen, dtype=torch.float32) / math.sqrt(latent_dim)
+    return w.to(torch.bfloat16)
+
+
 def causal_pairs(n, p) -> int:
     """Visible (query, key) pairs: every new token sees its prefix and itself."""
     n = np.asarray(n, dtype=np.int64)

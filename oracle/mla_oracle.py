@@ -507,7 +507,7 @@ def mla_prefill_rows_split(rows, q_nope, q_rope, k_nope, v, cache_lengths, valid
 
 
 def latent_up(cache, layer_idx, page_table, page_size, buffer_row_offsets_r, cache_offsets_r, latent_col,
-              latent_dim, w_kv, heads, cap):
+              latent_dim, w_kv, heads, cap, slots=None):
     """Per-head K_nope and V of one buffer row from the latent cache, float64.
 
     The pages call the cache a latent cache ("mla_prefill_v2_ragged", Args: the
@@ -520,14 +520,17 @@ def latent_up(cache, layer_idx, page_table, page_size, buffer_row_offsets_r, cac
     with w_kv [heads*256][latent_dim] (per head, 128 key rows then 128 value
     rows) and c_g the latent of the cache position that buffer slot g holds
     under the plan row (``gather``).  Returns (k_nope, v), each [cap, heads,
-    128]; slots the row does not use are 0.
+    128]; slots the row does not use are 0.  With ``slots`` (a list of slot
+    indices) only those slots are computed: [len(slots), heads, 128] each.
     """
     lat = gather(cache, layer_idx, page_table, page_size, buffer_row_offsets_r, cache_offsets_r,
                  latent_col, latent_dim, np.zeros((cap, latent_dim)))
     lat = np.asarray(lat, dtype=np.float64)
     used = int(np.asarray(_host_array(buffer_row_offsets_r), dtype=np.int64)[-1])
     lat[used:] = 0.0
+    if slots is not None:
+        lat = lat[np.asarray(slots, dtype=np.int64)]
     w = _as_f64(w_kv).reshape(heads, 2, NOPE_DEPTH, latent_dim)
-    kv = np.einsum("gc,hpdc->gphd", lat, w)            # [cap, 2, heads, 128]
+    kv = np.einsum("gc,hpdc->gphd", lat, w, optimize=True)   # [slots, 2, heads, 128]
     return kv[:, 0], kv[:, 1]
 

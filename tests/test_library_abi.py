@@ -23,12 +23,12 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail(f"{LIB} not built: run python -m mla_ragged_paged_amd.build")
+        pytest.fail(f"{LIB} not built: run python mla_ragged_paged_amd/build.py")
     return ctypes.CDLL(LIB)
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_merge",
+    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_latent_up", "mla_prefill_merge",
                                     "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_lse",
                                     "mla_prefill_ragged_row", "mla_prefill_ragged_split", "mla_status_string"]
 
@@ -133,6 +133,19 @@ def test_lse_and_merge_validation_without_gpu():
     assert lib.mla_prefill_ragged_split(*split_args(rows=ctypes.c_void_p(24))) == 2   # misaligned rope rows
     s.dtype = 1
     assert lib.mla_prefill_ragged_split(*split_args(rows=None)) == 3          # bf16 q_nope with an e4m3 cache
+    s.dtype = 0
+
+    def lat_args(**kw):
+        return [ref, 0, kw.get("b", 1), dummy, dummy, kw.get("col", 0), kw.get("dim", 64), kw.get("w", dummy), 2,
+                kw.get("cap", 4), dummy, dummy, None]
+    assert lib.mla_prefill_latent_up(*lat_args(w=None)) == 1
+    assert lib.mla_prefill_latent_up(*lat_args(dim=48)) == 2                # not a multiple of 64
+    assert lib.mla_prefill_latent_up(*lat_args(col=8)) == 2                 # window past the 64-wide row
+    assert lib.mla_prefill_latent_up(*lat_args(b=8193)) == 2
+    assert lib.mla_prefill_latent_up(*lat_args(w=ctypes.c_void_p(24))) == 2
+    assert lib.mla_prefill_latent_up(*lat_args(b=0)) == 0                   # empty batch: a no-op
+    s.dtype = 1
+    assert lib.mla_prefill_latent_up(*lat_args()) == 3                      # e4m3 cache
     s.dtype = 0
 
     def merge_args(**kw):

@@ -111,3 +111,15 @@ def test_unused_slots_are_zero_and_rows_follow_the_plan():
         k, v = _call(common, row, w, geo["latent_col"], geo["latent_dim"], geo["heads"], cap)
         used = int(row["cache_row_offsets"][-1])
         assert not k[used:].any() and not v[used:].any()
+
+
+def test_selected_slots_match_full_output():
+    common, rows, w, geo = _problem(914, [4, 2], [3, 5], cap=5)
+    for row in rows:
+        cap = row["k_nope"].shape[0]
+        k, v = _call(common, row, w, geo["latent_col"], geo["latent_dim"], geo["heads"], cap)
+        picks = [cap - 1, 0, 2]
+        ks, vs = oracle.latent_up(common["cache"], 0, common["page_table"], common["page_size"],
+                                  row["cache_row_offsets"], row["cache_offsets"], geo["latent_col"],
+                                  geo["latent_dim"], w, geo["heads"], cap, slots=picks)
+        assert np.array_equal(ks, k[picks]) and np.array_equal(vs, v[picks])
