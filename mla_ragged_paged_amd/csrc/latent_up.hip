@@ -11,29 +11,33 @@
 //
 // A dense contraction, so it runs on the 32x32x16 bf16 MFMA: C^T = W . L^T with
 // W rows as the A operand and the gathered latent rows as B.  A workgroup of
-// four waves owns a 128 (output features) x 128 (buffer slots) tile; an output
-// tile of 128 features is exactly the key or the value half of one head, so its
-// rows are 256-byte runs of K_nope or V.  Each wave owns 64 x 64 (2 x 2 MFMA
-// tiles).  The reduction runs in chunks of 64 latent columns through two LDS
-// stages of 32 KB (W tile 16 KB, latent tile 16 KB), filled by direct-to-LDS
-// buffer loads: W rows by plain offsets, latent rows through the page table
-// (each lane resolves its four slots' cache rows once, from the plan row kept
-// in LDS).  16-byte chunks are XOR-swizzled by (row / 2) % 8 so the operand
-// reads are free of bank conflicts.  The epilogue rounds to bf16, transposes
-// through LDS and writes whole 256-byte rows.
+// eight waves owns 256 output features (one head: its 128 key rows and 128
+// value rows) x 256 buffer slots, so every weight and latent row it stages
+// serves 256 outputs and the L2 -> LDS traffic is 1/128 byte per FLOP (a
+// 128 x 128 tile, measured at 15-20 % lower throughput, moves twice that).  Each wave owns
+// 128 features x 64 slots (4 x 2 MFMA tiles, 128 accumulator VGPRs).  The
+// reduction runs in chunks of 64 latent columns through two LDS stages of
+// 64 KB (weights 32 KB, latent 32 KB), filled by direct-to-LDS buffer loads:
+// weight rows by plain offsets, latent rows through the page table (each lane
+// resolves its four slots' cache rows once, from the plan row kept in LDS).
+// 16-byte chunks are XOR-swizzled by (row / 2) % 8, which keeps the operand
+// reads free of bank conflicts; operand fragments are read one k-step ahead of
+// their MFMAs.  The epilogue rounds to bf16, transposes through LDS and writes
+// whole 256-byte rows of K_nope and V.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace mla {
 namespace {
 
-constexpr int LT = 128;               // tile edge (features and slots)
+constexpr int TF = 256;               // features per tile (one head: 128 key + 128 value rows)
+constexpr int TS = 256;               // slots per tile
 constexpr int KC = 64;                // latent columns per chunk
-constexpr int NTH = 256;
-constexpr int A_OFF = 0;              // W tile   [128 rows][8 chunks of 16 B]
-constexpr int B_OFF = LT * KC * 2;    // latent   [128 rows][8 chunks]
-constexpr int LSTAGE = 2 * LT * KC * 2;   // 32 KiB
-constexpr int LLDS = 2 * LSTAGE;          // 64 KiB (also holds the plan row, then the output tile)
+constexpr int NTH = 512;              // 8 waves
+constexpr int A_OFF = 0;              // W tile      [256 rows][8 chunks of 16 B] 32 KiB
+constexpr int B_OFF = TF * KC * 2;    // latent tile [256 rows][8 chunks]          32 KiB
+constexpr int LSTAGE = (TF + TS) * KC * 2;   // 64 KiB
+constexpr int LLDS = 2 * LSTAGE;             // 128 KiB
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
@@ -47,25 +51,34 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(NTH, 2) latent_up_kernel(LatentArgs a) {
+__global__ void __launch_bounds__(NTH, 1) latent_up_kernel(LatentArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LLDS];
 
-  // ---- tile: XCD x takes a contiguous range of feature tiles (its L2 keeps
-  // their W rows) and walks the slot tiles; the 32 feature tiles of one slot
-  // tile run side by side and share its latent rows.
-  const uint32_t nt = 2 * a.heads;                 // feature tiles: (head, key | value)
+  // ---- tile.  XCD x (workgroup id % 8) takes a contiguous eighth of the heads.
+  // Within it, tiles run in blocks of up to 8 heads x 8 slot tiles (head
+  // fastest), so the 32 workgroups an XCD runs at once share 2 MB of weight rows
+  // and 2 MB of latent rows, both held by its 4 MB L2.
+  const uint32_t nt = a.heads;                     // feature tiles: one per head
+  const uint32_t mtn = (a.cap + TS - 1) / TS;      // slot tiles
   const uint32_t bid = blockIdx.x;
   uint32_t ft, mt;
-  if ((nt & 7u) == 0) {
-    const uint32_t per = nt >> 3, j = bid >> 3;
-    ft = (bid & 7u) * per + j % per;
-    mt = j / per;
-  } else {
-    ft = bid % nt;
-    mt = bid / nt;
+  {
+    const bool split8 = (nt & 7u) == 0;
+    const uint32_t per = split8 ? nt >> 3 : nt;
+    const uint32_t f_base = split8 ? (bid & 7u) * per : 0u;
+    const uint32_t j = split8 ? bid >> 3 : bid;
+    const uint32_t gf = min(per, 8u), gm = 8u;
+    const uint32_t mg = j / (per * gm);
+    const uint32_t r = j - mg * per * gm;
+    const uint32_t gml = min(gm, mtn - mg * gm);
+    const uint32_t fg = r / (gf * gml);
+    const uint32_t gfl = min(gf, per - fg * gf);
+    const uint32_t q = r - fg * gf * gml;
+    ft = f_base + fg * gf + q % gfl;
+    mt = mg * gm + q / gfl;
   }
   const uint32_t used = a.bro[a.batch];            // slots this plan row fills
-  const uint32_t m0 = mt * LT;
+  const uint32_t m0 = mt * TS;
   if (m0 >= used) return;
 
   const int tid = threadIdx.x;
@@ -99,9 +112,9 @@ __global__ void __launch_bounds__(NTH, 2) latent_up_kernel(LatentArgs a) {
 
   // ---- load slots: load u of wave w covers tile rows 32w + 8u .. +7; lane ->
   // row 32w + 8u + lane/8, stored chunk lane%8 holds source chunk (lane%8) ^ swz(row)
-  const uint32_t n0 = ft * LT;
+  const uint32_t n0 = ft * TF;
   const uint32_t kdim = a.latent_dim;
-  const auto w_rs = rsrc(a.w + (size_t)n0 * kdim, LT * kdim * 2);
+  const auto w_rs = rsrc(a.w + (size_t)n0 * kdim, TF * kdim * 2);
   const auto c_rs = rsrc(a.cache, a.cache_bytes);
   uint32_t a_off[4], b_src[4];
 #pragma unroll
@@ -122,23 +135,26 @@ __global__ void __launch_bounds__(NTH, 2) latent_up_kernel(LatentArgs a) {
   };
 
   // ---- operand reads: wave (wn, wm) = (w & 1, w >> 1) owns features
-  // 64wn .. +63 and slots 64wm .. +63; fragment x of k-step ks is row
+  // 128wn .. +127 and slots 64wm .. +63; fragment x of k-step ks is row
   // base + 32x + li, columns 16ks + 8hf .. +7
   const int wn = w & 1, wm = w >> 1;
-  uint32_t a_rd[2][4], b_rd[2][4];
+  uint32_t a_rd[4][4], b_rd[2][4];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int ra = 64 * wn + 32 * x + li, rb = 64 * wm + 32 * x + li;
+  for (int x = 0; x < 4; ++x) {
+    const int ra = 128 * wn + 32 * x + li;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      a_rd[x][ks] = A_OFF + ra * 128 + 16 * ((2 * ks + hf) ^ swz(ra));
-      b_rd[x][ks] = B_OFF + rb * 128 + 16 * ((2 * ks + hf) ^ swz(rb));
-    }
+    for (int ks = 0; ks < 4; ++ks) a_rd[x][ks] = A_OFF + ra * 128 + 16 * ((2 * ks + hf) ^ swz(ra));
+  }
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int rb = 64 * wm + 32 * y + li;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) b_rd[y][ks] = B_OFF + rb * 128 + 16 * ((2 * ks + hf) ^ swz(rb));
   }
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
 
@@ -151,51 +167,58 @@ __global__ void __launch_bounds__(NTH, 2) latent_up_kernel(LatentArgs a) {
     __syncthreads();
     if (kc + 1 < nkc) issue(kc + 1, stage ^ 1);
     const uint8_t* st = lds + stage * LSTAGE;
+    // fragments of k-step ks + 1 are read while the MFMAs of ks run
+    bf16x8 fa[2][4], fb[2][2];
+    auto rd = [&](int ks, int slot) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) fa[slot][x] = *reinterpret_cast<const bf16x8*>(st + a_rd[x][ks]);
+#pragma unroll
+      for (int y = 0; y < 2; ++y) fb[slot][y] = *reinterpret_cast<const bf16x8*>(st + b_rd[y][ks]);
+    };
+    rd(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 fa[2], fb[2];
+      if (ks + 1 < 4) rd(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        fa[x] = *reinterpret_cast<const bf16x8*>(st + a_rd[x][ks]);
-        fb[x] = *reinterpret_cast<const bf16x8*>(st + b_rd[x][ks]);
-      }
+      for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(fa[x], fb[y], acc[x][y]);
+        for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(fa[ks & 1][x], fb[ks & 1][y], acc[x][y]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- epilogue: acc[x][y][i] is feature 64wn + 32x + 8(i/4) + 4hf + i%4 of
+  // ---- epilogue: acc[x][y][i] is feature 128wn + 32x + 8(i/4) + 4hf + i%4 of
   // slot 64wm + 32y + li.  Round to bf16 and write the tile as [slot][feature]
-  // (256 B per slot, 16-byte chunk c at c ^ (slot % 16)), then store whole rows.
+  // (512 B per slot: key 256 B then value 256 B; 16-byte chunk c at c ^ (slot % 32)),
+  // then store whole rows.
   __syncthreads();                                  // every wave is done reading the stages
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int r = 64 * wm + 32 * y + li;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int f = 64 * wn + 32 * x + 8 * q + 4 * hf;      // 4 consecutive features
+        const int f = 128 * wn + 32 * x + 8 * q + 4 * hf;
         const uint32_t w0 = pack_bf16x2(acc[x][y][4 * q], acc[x][y][4 * q + 1]);
         const uint32_t w1 = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
-        const int chunk = (f >> 3) ^ (r & 15);
-        *reinterpret_cast<MLA_LDS u32x2*>((MLA_LDS uint8_t*)lds + r * 256 + 16 * chunk + 2 * (f & 7)) =
+        const int chunk = (f >> 3) ^ (r & 31);
+        *reinterpret_cast<MLA_LDS u32x2*>((MLA_LDS uint8_t*)lds + r * 512 + 16 * chunk + 2 * (f & 7)) =
             u32x2{w0, w1};
       }
     }
   __syncthreads();
-  const uint32_t head = ft >> 1;
-  uint16_t* dst = (ft & 1u) ? a.v : a.k_nope;
-  const size_t row_stride = (size_t)a.heads * 128;   // elements per slot in K_nope / V
+  const uint32_t head = ft;
+  const size_t row_stride = (size_t)a.heads * 128;
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = 16 * it + (tid >> 4), c = tid & 15;
+  for (int it = 0; it < 16; ++it) {
+    const int r = 16 * it + (tid >> 5), c = tid & 31;    // 32 chunks per slot: 16 key + 16 value
     const uint32_t g = m0 + r;
     if (g < used) {
-      const i32x4 val = *reinterpret_cast<const MLA_LDS i32x4*>((MLA_LDS uint8_t*)lds + r * 256 + 16 * (c ^ (r & 15)));
-      st16(dst + g * row_stride + head * 128 + c * 8, val);
+      const i32x4 val = *reinterpret_cast<const MLA_LDS i32x4*>((MLA_LDS uint8_t*)lds + r * 512 + 16 * (c ^ (r & 31)));
+      uint16_t* dst = (c < 16 ? a.k_nope : a.v) + g * row_stride + head * 128 + (c & 15) * 8;
+      st16(dst, val);
     }
   }
 }
@@ -203,8 +226,8 @@ __global__ void __launch_bounds__(NTH, 2) latent_up_kernel(LatentArgs a) {
 }  // namespace
 
 hipError_t launch_latent_up(const LatentArgs& a, hipStream_t stream) {
-  const uint64_t mt = (a.cap + LT - 1) / LT;
-  const uint64_t grid = mt * 2 * a.heads;
+  const uint64_t mt = (a.cap + TS - 1) / TS;
+  const uint64_t grid = mt * a.heads;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(latent_up_kernel, dim3((uint32_t)grid), dim3(NTH), 0, stream, a);
   return hipGetLastError();
