@@ -30,6 +30,8 @@ CASES = [
     dict(n=[150, 70], p=[33, 0], heads=2, ps=48, cap=None, dim=512, col=0),     # page size not a power of two
     dict(n=[40, 7], p=[10, 3], heads=5, ps=1, cap=23, dim=128, col=64),         # one token per page, narrow latent
     dict(n=[130, 40, 0, 200], p=[10, 0, 5, 64], heads=16, ps=16, cap=300, dim=512, col=0),
+    dict(n=[0, 90, 0, 33], p=[0, 0, 0, 500], heads=8, ps=64, cap=1000, dim=256, col=256),   # empty contexts, spare slots
+    dict(n=[300, 5], p=[700, 0], heads=12, ps=32, cap=257, dim=512, col=0),     # 12 heads, tiles past the fill
 ]
 
 

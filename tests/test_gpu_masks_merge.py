@@ -39,6 +39,7 @@ CASES = [
     dict(n=[150, 70], p=[33, 0], heads=2, ps=48),           # page size not a power of two
     dict(n=[513], p=[0], heads=2, ps=128),                  # 4 full query tiles + 1 row
     dict(n=[130, 40, 0, 200], p=[10, 0, 5, 64], heads=16, ps=16),
+    dict(n=[0, 300, 0, 7], p=[900, 0, 0, 1500], heads=8, ps=128),     # contexts without new tokens, empty ones
 ]
 
 
@@ -107,7 +108,7 @@ def test_lse_and_fp32_output_every_output(case, dtype, mask):
 
 MULTI = [
     dict(case=0, cap=300), dict(case=0, cap=97), dict(case=1, cap=512), dict(case=2, cap=64),
-    dict(case=3, cap=200), dict(case=4, cap=128),
+    dict(case=3, cap=200), dict(case=4, cap=128), dict(case=5, cap=700),
 ]
 
 

@@ -166,3 +166,33 @@ def test_full_size_split_sampled(name, rope):
     got = np.stack([got_all[t, h].cpu().numpy() for t, h in rows])
     bar = BAR[w.spec.dtype]
     assert report(got, ref, bar, f"{name}-split-{rope}") <= bar
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("heads", [8, 24])
+def test_split_one_plan_row_of_several(dtype, heads):
+    """A later row of a multi-row plan (cache_offsets non-zero, keys after some
+    queries) with 8 and 24 heads, paged K_rope, against the oracle on that row."""
+    spec = workloads.Spec("splitrow", 3, (0, 0), (0, 0), heads, 16, True, dtype, row_width=576, rope_col=512,
+                          seed=840 + heads)
+    w = workloads.build(spec, n=[90, 20, 150], p=[60, 0, 200])
+    step = PrefillStep(w, "cuda", cap=160)
+    step.plan()
+    torch.cuda.synchronize()
+    bro, co, _ = check_plan(step, w)
+    q_nope, q_rope = workloads.split_query(w)
+    sc = step.scales or {}
+    for r in (1, step.rows - 1):
+        kn, v = step.row_buffers(r)
+        out = torch.full((w.total_q, w.heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+        m.mla_prefill_ragged_split(out, q_nope.cuda(), q_rope.cuda(), kn, v, step.kv, 0, step.input_row_offsets,
+                                   step.buffer_row_offsets[r], step.cache_offsets[r], w.softmax_scale,
+                                   q_scale=sc.get("q"), k_scales=sc.get("k_nope"), v_scale=sc.get("v"),
+                                   q_max_seq_len=w.max_q)
+        torch.cuda.synchronize()
+        used = max(1, int(bro[r][-1]))
+        ref = oracle.mla_prefill_ragged_split(
+            q_nope, q_rope, kn[:used].cpu(), v[:used].cpu(), w.cache_lengths, w.input_row_offsets, bro[r], co[r],
+            w.softmax_scale, cache=w.cache, layer_idx=0, page_table=w.page_table, page_size=w.spec.page_size,
+            rope_col=w.spec.rope_col, scales=w.scales)
+        assert report(out.cpu().numpy(), ref, BAR[dtype], f"splitrow-{dtype}-h{heads}-r{r}") <= BAR[dtype]

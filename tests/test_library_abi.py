@@ -158,3 +158,30 @@ def test_lse_and_merge_validation_without_gpu():
     assert lib.mla_prefill_merge(*merge_args(oa=ctypes.c_void_p(20))) == 2
     assert lib.mla_prefill_merge(*merge_args(lb=ctypes.c_void_p(18))) == 2
     assert lib.mla_prefill_merge(*merge_args(t=0)) == 0                    # empty: a no-op
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    """The product path has no fallback: importing the package without its HIP
+    library raises ImportError (a copy of the package sources, no library)."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "mla_ragged_paged_amd")
+    dst = tmp_path / "mla_ragged_paged_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "*.so.tmp", "__pycache__", "csrc"))
+    assert not any(p.suffix == ".so" for p in dst.iterdir())
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import mla_ragged_paged_amd\nexcept ImportError as e:\n    print('ImportError:', e); sys.exit(3)\n"
+            "sys.exit(0)\n") % str(tmp_path)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 3, res.stdout + res.stderr
+    assert "is missing" in res.stdout
+
+
+def test_first_build_needs_no_library():
+    """The build entry point loads the build script by path, so it does not import
+    the package (which would load the library it is about to build)."""
+    text = open(os.path.join(ROOT, "__graft_entry__.py")).read()
+    build_src = text[text.index("def build()"):text.index("def smoke()")]
+    assert "spec_from_file_location" in build_src
+    assert "from mla_ragged_paged_amd import build" not in build_src
