@@ -14,6 +14,8 @@
  *                       "flare_mla_prefill"; launch shape and argument meanings
  *                       of page "mla_prefill_v2_ragged").
  *
+ * The other calls widen that step:
+ *
  *   mla_prefill_ragged_split  the same attention for a query given in two parts,
  *                       q_nope and q_rope, and K_rope from the cache or from
  *                       contiguous rows (page "flare_mla_prefill", the q_nope /
