@@ -248,6 +248,17 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
                             "latent_step_median_ms": round(med_step, 4)}
         del ls
 
+    # the whole step captured as a HIP graph and replayed, against eager launches
+    from mla_ragged_paged_amd.pipeline import CapturedStep
+    out["graph_step"] = {}
+    for wl in (w, workloads.build(workloads.SPECS["tiny"])):
+        gs = PrefillStep(wl, "cuda:0")
+        cs = CapturedStep(gs)
+        med_e, _ = _median_ms(torch, gs.run, reps, stream)
+        med_g, _ = _median_ms(torch, cs.replay, reps, stream)
+        out["graph_step"][wl.spec.name] = {"eager_median_ms": round(med_e, 4), "graph_median_ms": round(med_g, 4)}
+        del cs, gs
+
     T, H = 16384, 128
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev).manual_seed(12)

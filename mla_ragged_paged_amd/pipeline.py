@@ -137,3 +137,31 @@ class PrefillStep:
                 self.attention(0, k_nope=kn, v=v, stream=stream)
             else:
                 self.attention_row_merged(r, stream)
+
+
+class CapturedStep:
+    """One ``PrefillStep.run()`` captured as a HIP graph and replayed.
+
+    The step's kernels are recorded once on a side stream (torch's graph
+    capture, which drives hipStreamBeginCapture / hipGraphInstantiate); a replay
+    launches the whole step -- plan, then per buffer row its gather or latent
+    decompression and its attention -- with one graph launch and no per-kernel
+    host work.  The step's device buffers are the graph's: inputs are changed
+    by writing into ``step``'s tensors in place.  None of the captured kernels
+    issues a memset.
+    """
+
+    def __init__(self, step: PrefillStep, warmup: int = 2):
+        self.step = step
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                step.run()
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            step.run()
+
+    def replay(self):
+        self.graph.replay()
