@@ -377,7 +377,15 @@ def main():
     }
     if dtype == "fp8":
         result["pct_of_fp8_peak"] = round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 2)
-    if not args.no_extras:
+    def guarded(name, fn):
+        """A side measurement; its failure is reported in the line instead of losing the line."""
+        try:
+            result[name] = fn()
+        except Exception as e:  # noqa: BLE001 -- any failure of a side measurement
+            result[name] = {"error": f"{type(e).__name__}: {e}"}
+            print(f"[bench] {name} failed: {e!r}", file=sys.stderr, flush=True)
+
+    def cold_cache():
         # attention with L2 and MALL flushed by a 512 MiB write before each launch
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
         cold = []
@@ -391,16 +399,19 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del flush
         cold.sort()
-        result["cold_cache"] = {"flush_mib": 512, "attention_median_ms": round(cold[len(cold) // 2], 4),
-                                "attention_min_ms": round(cold[0], 4),
-                                "achieved_TFLOPs_median": round(flops / (cold[len(cold) // 2] * 1e-3) / 1e12, 2)}
+        return {"flush_mib": 512, "attention_median_ms": round(cold[len(cold) // 2], 4),
+                "attention_min_ms": round(cold[0], 4),
+                "achieved_TFLOPs_median": round(flops / (cold[len(cold) // 2] * 1e-3) / 1e12, 2)}
+
+    if not args.no_extras:
+        guarded("cold_cache", cold_cache)
         print("[bench] gather bandwidth on a >= 1 GiB paged cache", file=sys.stderr, flush=True)
-        result["gather_bench"] = gather_bench(torch)
-        print("[bench] null mask, three buffer rows merged, merge kernel", file=sys.stderr, flush=True)
-        result["next_rows"] = next_rows_bench(torch, w, attn_median)
+        guarded("gather_bench", lambda: gather_bench(torch))
+        print("[bench] null mask, buffer rows, split query, decompression, graphs, merge", file=sys.stderr, flush=True)
+        guarded("next_rows", lambda: next_rows_bench(torch, w, attn_median))
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        guarded("cpu_baseline", lambda: cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(result), flush=True)
 
 
