@@ -172,7 +172,7 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
     partials."""
     from mla_ragged_paged_amd import _binding as B
     from mla_ragged_paged_amd import workloads
-    from mla_ragged_paged_amd.pipeline import PrefillStep
+    from mla_ragged_paged_amd.pipeline import PrefillStep, balanced_split_keys
     stream = torch.cuda.current_stream()
     peak = PEAK_TFLOPS[w.spec.dtype]
     out = {}
@@ -247,6 +247,35 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
                             "frac_of_peak": round(fl_up / (med_up * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
                             "latent_step_median_ms": round(med_step, 4)}
         del ls
+
+    # one GPU's share of the same batch under 8-way head parallelism: 16 heads,
+    # the same sequence lengths (the work-unit count, not the arithmetic, changes)
+    import dataclasses
+    share = workloads.build(dataclasses.replace(w.spec, name=w.spec.name + "_h16", heads=w.heads // 8))
+    ss = PrefillStep(share, "cuda:0")
+    ss.run()
+    med, best = _median_ms(torch, lambda: ss.attention(0), reps, stream)
+    fl = workloads.causal_flops(share.n, share.p, share.heads)
+    out["tp8_share"] = {"heads": share.heads, "tflop": round(fl / 1e12, 5), "attention_median_ms": round(med, 4),
+                        "attention_min_ms": round(best, 4), "achieved_TFLOPs": round(fl / (med * 1e-3) / 1e12, 2),
+                        "frac_of_peak": round(fl / (med * 1e-3) / 1e12 / peak, 4),
+                        "split_keys": balanced_split_keys(share.n, share.p, share.heads)}
+    del ss
+
+    # 8 heads (16-way head parallelism): fewer query tiles than workgroup slots, where
+    # the key split (mla_prefill_ragged_kvsplit, attention + merge pass) is chosen
+    share8 = workloads.build(dataclasses.replace(w.spec, name=w.spec.name + "_h8", heads=w.heads // 16))
+    sk8 = balanced_split_keys(share8.n, share8.p, share8.heads)
+    fl8 = workloads.causal_flops(share8.n, share8.p, share8.heads)
+    row = {"heads": share8.heads, "tflop": round(fl8 / 1e12, 5), "split_keys": sk8}
+    for label, sk in (("plain", 0), ("kvsplit", sk8)):
+        st8 = PrefillStep(share8, "cuda:0", split_keys=sk)
+        st8.run()
+        med, _ = _median_ms(torch, lambda: st8.attention(0), reps, stream)
+        row[f"{label}_median_ms"] = round(med, 4)
+        row[f"{label}_TFLOPs"] = round(fl8 / (med * 1e-3) / 1e12, 2)
+        del st8
+    out["tp16_share"] = row
 
     # the whole step captured as a HIP graph and replayed, against eager launches
     from mla_ragged_paged_amd.pipeline import CapturedStep

@@ -24,6 +24,10 @@
  *   mla_prefill_latent_up  per-head K_nope / V of one buffer row, up-projected
  *                       from the latent part of the cache rows the plan row holds.
  *
+ *   mla_prefill_ragged_kvsplit  the attention of mla_prefill_ragged with the
+ *                       key range of long query tiles split over two workgroups
+ *                       and merged (for grids with few tiles, e.g. few heads).
+ *
  * When the plan cuts the contexts over several buffer rows, each row's
  * attention covers part of a sequence's keys:
  *
@@ -344,6 +348,54 @@ mla_status_t mla_prefill_ragged_split(void* output, mla_dtype_t output_dtype, fl
                                       uint32_t batch_size, uint32_t total_q_tokens, uint32_t num_heads,
                                       uint32_t depth, mla_mask_t mask, float scale, uint32_t q_max_seq_len,
                                       void* stream);
+
+/*
+ * mla_prefill_ragged_kvsplit -- the attention of mla_prefill_ragged (page
+ * "flare_mla_prefill", description and Args), with the log-sum-exp of
+ * mla_prefill_ragged_lse, scheduled for batches with few query tiles per head
+ * count (for instance one GPU's share of the heads under tensor parallelism).
+ * The pages fix what is computed, not how the work is cut; this call cuts it by
+ * the split-KV scheme published as Flash-Decoding (Dao, Haziza, Massa, Sizov,
+ * 2023): a 128-query tile of one sequence and head whose visible keys number
+ * more than split_keys is computed by two workgroups, one per half of its
+ * 64-key tiles, each writing its normalised fp32 partial and log-sum-exp to
+ * `workspace`; a second kernel on the same stream combines the two as
+ * mla_prefill_merge does.  Other tiles are computed whole, as in
+ * mla_prefill_ragged.  The result equals mla_prefill_ragged's up to fp32
+ * rounding order (the partials are fp32; a bf16 output is rounded once, after
+ * the combine).
+ *
+ * All arguments up to q_max_seq_len are those of mla_prefill_ragged_lse
+ * without prev_output / prev_lse, with the same meaning and checks; lse may
+ * be NULL.
+ *   split_keys       [host] 0: no tile is split (workspace is not used); else
+ *                    at least 128.  A smaller value splits more tiles.
+ *   workspace        device fp32, 16-byte aligned, at least
+ *                    mla_prefill_kvsplit_workspace_bytes(total_q_tokens,
+ *                    num_heads) bytes; owned by the caller, contents on entry
+ *                    ignored, contents on exit unspecified; must not overlap
+ *                    any other argument.  May be NULL when split_keys is 0.
+ *   workspace_bytes  [host] its size in bytes.
+ * Two calls that share a workspace must be ordered (one stream, or events).
+ * Errors: those of mla_prefill_ragged_lse; NULL_ARG for a NULL workspace with
+ * split_keys > 0; BAD_SHAPE for split_keys in 1..127, a workspace that is too
+ * small or not 16-byte aligned.
+ */
+mla_status_t mla_prefill_ragged_kvsplit(void* output, mla_dtype_t output_dtype, float* lse, const void* q,
+                                        mla_dtype_t qkv_dtype, const void* k_nope, const void* v,
+                                        const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                        const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                        const uint32_t* cache_offsets, uint32_t batch_size,
+                                        uint32_t total_q_tokens, uint32_t num_heads, uint32_t q_depth,
+                                        uint32_t depth, mla_mask_t mask, float scale, const float* q_scale,
+                                        const float* k_nope_scale, const float* v_scale, uint32_t q_max_seq_len,
+                                        uint32_t split_keys, float* workspace, uint64_t workspace_bytes,
+                                        void* stream);
+
+/* Workspace bytes mla_prefill_ragged_kvsplit needs: total_q_tokens * num_heads
+ * * (2 * 128 + 2) * 4 (two fp32 partial rows and two log-sum-exp values per
+ * token and head). */
+uint64_t mla_prefill_kvsplit_workspace_bytes(uint32_t total_q_tokens, uint32_t num_heads);
 
 /*
  * mla_prefill_ragged_row -- one buffer row of the plan of page

@@ -17,11 +17,13 @@ from ._binding import (  # noqa: F401
     PagedCache,
     library_path,
     mla_prefill_gather,
+    mla_prefill_kvsplit_workspace_bytes,
     mla_prefill_last_hip_error,
     mla_prefill_plan,
     mla_prefill_latent_up,
     mla_prefill_merge,
     mla_prefill_ragged,
+    mla_prefill_ragged_kvsplit,
     mla_prefill_ragged_lse,
     mla_prefill_ragged_row,
     mla_prefill_ragged_split,

@@ -73,6 +73,12 @@ def _load():
     lib.mla_prefill_ragged_split.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, cp, u32, vp, vp, vp,
                                              u32, u32, u32, u32, i32, ctypes.c_float, u32, vp]
     lib.mla_prefill_ragged_split.restype = i32
+    lib.mla_prefill_ragged_kvsplit.argtypes = [vp, i32, vp, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32, u32, u32,
+                                               u32, i32, ctypes.c_float, vp, vp, vp, u32, u32, vp, ctypes.c_uint64,
+                                               vp]
+    lib.mla_prefill_ragged_kvsplit.restype = i32
+    lib.mla_prefill_kvsplit_workspace_bytes.argtypes = [u32, u32]
+    lib.mla_prefill_kvsplit_workspace_bytes.restype = ctypes.c_uint64
     lib.mla_prefill_latent_up.argtypes = [cp, u32, u32, vp, vp, u32, u32, vp, u32, u32, vp, vp, vp]
     lib.mla_prefill_latent_up.restype = i32
     lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
@@ -246,6 +252,35 @@ def mla_prefill_ragged_lse(output, lse, q, k_nope, v, k_rope: PagedCache, layer_
                                        k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
                                        _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
            "mla_prefill_ragged_lse")
+
+
+def mla_prefill_kvsplit_workspace_bytes(total_q_tokens: int, num_heads: int) -> int:
+    """Bytes of the fp32 workspace mla_prefill_ragged_kvsplit needs for T tokens and H heads."""
+    return int(_lib.mla_prefill_kvsplit_workspace_bytes(int(total_q_tokens), int(num_heads)))
+
+
+def mla_prefill_ragged_kvsplit(output, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length,
+                               cache_row_offsets, cache_offsets, scale, split_keys, workspace, lse=None,
+                               q_scale=None, k_nope_scale=None, v_scale=None, q_max_seq_len=0, stream=None,
+                               mask="causal"):
+    """The attention of mla_prefill_ragged (and its log-sum-exp lse [T, H] when given) with
+    each 128-query tile that sees more than ``split_keys`` keys computed as two halves of its
+    key tiles and merged; ``workspace`` is a float32 tensor of at least
+    mla_prefill_kvsplit_workspace_bytes(T, H) bytes (unused when split_keys is 0)."""
+    T, H, qd = q.shape
+    _contiguous(output=output, lse=lse, q=q, k_nope=k_nope, v=v, workspace=workspace)
+    _shapes(T, H, rows=[("output", output)], lses=[("lse", lse)])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = k_rope.as_struct()
+    _check(_lib.mla_prefill_ragged_kvsplit(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _ptr(q),
+                                           _dtype_code(q), _ptr(k_nope), _ptr(v), ctypes.byref(s), layer_idx,
+                                           _idx(valid_length, "valid_length"),
+                                           _idx(cache_row_offsets, "cache_row_offsets"),
+                                           _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H,
+                                           qd, k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
+                                           _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), int(split_keys),
+                                           _f32(workspace, "workspace"), nbytes, _stream(stream)),
+           "mla_prefill_ragged_kvsplit")
 
 
 def mla_prefill_ragged_row(output, acc, acc_lse, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length,

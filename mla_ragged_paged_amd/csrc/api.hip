@@ -123,6 +123,14 @@ struct QuerySource {
   bool split;
 };
 
+// Key split of a call: tiles seeing more than split_keys keys are computed in two
+// halves into the workspace and merged (split_keys 0: none).
+struct KvSplit {
+  uint32_t split_keys;
+  float* workspace;
+  uint64_t workspace_bytes;
+};
+
 // Shared validation and launch of the attention entry points.
 mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, const float* prev_output,
                           const float* prev_lse, float* acc, float* acc_lse, bool row_mode, const QuerySource& qs,
@@ -131,8 +139,14 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
                           const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
                           uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
                           const float* q_scale, const float* k_nope_scale, const float* v_scale,
-                          uint32_t q_max_seq_len, void* stream) {
+                          uint32_t q_max_seq_len, void* stream, const KvSplit& kvs = KvSplit{0u, nullptr, 0u}) {
   if (!output || !qs.q || !k_nope || !v || !valid_length || !cache_row_offsets) return MLA_ERR_NULL_ARG;
+  if (kvs.split_keys != 0) {
+    if (!kvs.workspace) return MLA_ERR_NULL_ARG;
+    if (kvs.split_keys < 128 || reinterpret_cast<uintptr_t>(kvs.workspace) % 16 ||
+        kvs.workspace_bytes < mla_prefill_kvsplit_workspace_bytes(total_q_tokens, num_heads))
+      return MLA_ERR_BAD_SHAPE;
+  }
   if (qs.split && !qs.q_rope) return MLA_ERR_NULL_ARG;
   if ((prev_output == nullptr) != (prev_lse == nullptr)) return MLA_ERR_NULL_ARG;
   if (row_mode && (!acc || !acc_lse)) return MLA_ERR_NULL_ARG;
@@ -184,7 +198,8 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
       (qs.split && (uint64_t)total_q_tokens * num_heads * 64 * 2 >= (1ull << 32)))
     return MLA_ERR_BAD_SHAPE;
   const uint32_t q_max = q_max_seq_len ? q_max_seq_len : total_q_tokens;
-  const uint64_t units = (uint64_t)num_heads * batch_size * ((q_max + 127) / 128);
+  // launch units (two per query tile with the key split), counted in 32 bits on the device
+  const uint64_t units = (uint64_t)num_heads * batch_size * ((q_max + 127) / 128) * (kvs.split_keys ? 2u : 1u);
   if (units > 0x7FFFFFF0ull) return MLA_ERR_BAD_SHAPE;
 
   mla::PrefillArgs a{};
@@ -225,6 +240,9 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
   a.v_scale = v_scale;
   a.batch = batch_size;
   a.heads = num_heads;
+  a.tokens = total_q_tokens;
+  a.split_keys = kvs.split_keys;
+  a.ws = kvs.workspace;
   a.scale = scale;
   {
     const float c = (scale < 0.f ? -scale : scale) * 1.4426950408889634f;
@@ -280,6 +298,27 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
                       v, k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
                       total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale,
                       q_max_seq_len, stream);
+}
+
+mla_status_t mla_prefill_ragged_kvsplit(void* output, mla_dtype_t output_dtype, float* lse, const void* q,
+                                        mla_dtype_t qkv_dtype, const void* k_nope, const void* v,
+                                        const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                        const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                        const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                        uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
+                                        float scale, const float* q_scale, const float* k_nope_scale,
+                                        const float* v_scale, uint32_t q_max_seq_len, uint32_t split_keys,
+                                        float* workspace, uint64_t workspace_bytes, void* stream) {
+  return prefill_impl(output, output_dtype, lse, nullptr, nullptr, nullptr, nullptr, false,
+                      QuerySource{q, nullptr, nullptr, false}, qkv_dtype, k_nope, v, k_rope, layer_idx,
+                      valid_length, cache_row_offsets, cache_offsets, batch_size, total_q_tokens, num_heads, q_depth,
+                      depth, mask, scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream,
+                      KvSplit{split_keys, workspace, workspace_bytes});
+}
+
+uint64_t mla_prefill_kvsplit_workspace_bytes(uint32_t total_q_tokens, uint32_t num_heads) {
+  // two partial rows of 128 fp32 and two log-sum-exp values per (token, head)
+  return (uint64_t)total_q_tokens * num_heads * (2u * 128u + 2u) * sizeof(float);
 }
 
 mla_status_t mla_prefill_ragged_split(void* output, mla_dtype_t output_dtype, float* lse, const void* q_nope,

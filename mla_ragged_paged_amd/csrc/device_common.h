@@ -184,4 +184,22 @@ __device__ __forceinline__ bool decode_unit(uint32_t bid, uint32_t H, uint32_t B
   return true;
 }
 
+// Key split, for grids with too few units to keep every CU busy until the end
+// (a few sequences at a few heads, where one long query tile outlasts the rest
+// of the grid): a query tile whose visible key range [0, jend) holds more than
+// split_keys keys is computed by two units, one per half of its key tiles, each
+// writing a normalised fp32 partial and its log-sum-exp to the workspace; a
+// second pass merges the two.  The attention kernels and the merge pass take
+// the decision from these same values.
+__device__ __forceinline__ bool kv_split_tile(int32_t jend, uint32_t split_keys) {
+  return split_keys != 0u && jend > (int32_t)split_keys;
+}
+
+// Workspace target of half c (0: first key tiles, 1: the rest) of a split tile:
+// partial rows at ws + c*T*H*128, their log-sum-exp at ws + 2*T*H*128 + c*T*H.
+__device__ __forceinline__ RowTarget kv_split_target(const PrefillArgs& a, uint32_t c) {
+  const size_t plane = (size_t)a.tokens * a.heads;
+  return RowTarget{a.ws + c * plane * 128, 1u, a.ws + 2 * plane * 128 + c * plane, nullptr, nullptr};
+}
+
 }  // namespace mla

@@ -71,6 +71,9 @@ struct PrefillArgs {
   const void* q_rope;                 // split Q: bf16 [T][H][64] (q then holds q_nope [T][H][128])
   const void* rope_rows;              // contiguous bf16 K_rope [rows][64] laid out like K, or nullptr (paged)
   uint32_t q_split;                   // 1: Q comes as q_nope (a.q) + q_rope
+  float* ws;                          // key split: [2][T][H][128] fp32 partial rows, then [2][T][H] lse
+  uint32_t split_keys;                // key split: tiles seeing more keys are split in two; 0 = none
+  uint32_t tokens;                    // T (key split: workspace plane size)
 };
 
 struct MergeArgs {
@@ -109,6 +112,7 @@ hipError_t launch_gather(const GatherArgs& a, int unit, hipStream_t stream);
 hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream);
 hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_kv_split_merge(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_latent_up(const LatentArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -79,16 +79,20 @@ __device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, uint32_t off
 // CAUSAL: causal mask, else the null mask.  PLAIN: bf16 output only (no
 // log-sum-exp, no earlier partial to merge).  QSPLIT: the query comes as q_nope
 // [T][H][128] and q_rope [T][H][64], and K_rope may be given as contiguous rows
-// laid out like K (else it is read through the page table).
-template <bool CAUSAL, bool PLAIN, bool QSPLIT>
+// laid out like K (else it is read through the page table).  KVSPLIT: the grid
+// holds two units per query tile, and a tile that kv_split_tile selects is
+// computed as two halves of its key tiles into the workspace (full query only).
+template <bool CAUSAL, bool PLAIN, bool QSPLIT, bool KVSPLIT>
 __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
-  // ---- work unit (XCD- and shader-engine-aware order, longest tiles first)
+  // ---- work unit (XCD- and shader-engine-aware order, longest tiles first).
+  // Key split: virtual tile 2qt + 1 (launched first) takes tile qt's first half,
+  // or the whole tile when it is not split; 2qt takes the second half.
   const uint32_t bid = blockIdx.x;
   WorkUnit u;
-  if (!decode_unit(bid, a.heads, a.batch, a.qtiles, u)) return;
-  const uint32_t h = u.h, b = u.b, qt = u.qt;
+  if (!decode_unit(bid, a.heads, a.batch, KVSPLIT ? 2u * a.qtiles : a.qtiles, u)) return;
+  const uint32_t h = u.h, b = u.b, qt = KVSPLIT ? u.qt >> 1 : u.qt;
   const uint32_t t0 = a.valid_length[b];
   const uint32_t n = a.valid_length[b + 1] - t0;
   const uint32_t i0 = qt * BM;
@@ -114,6 +118,18 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   constexpr bool causal = CAUSAL;
   const int32_t jend = causal ? max(0, min(p + i_last - c0 + 1, len)) : len;
   const int32_t nkt = (jend + BN - 1) / BN;
+  int32_t kt_lo = 0, kt_hi = nkt;                     // this unit's key tiles
+  bool part = false;                                  // key split: writes a partial
+  if constexpr (KVSPLIT) {
+    part = kv_split_tile(jend, a.split_keys);
+    const int32_t mid = (nkt + 1) >> 1;
+    if (part) {
+      kt_lo = (u.qt & 1u) ? 0 : mid;
+      kt_hi = (u.qt & 1u) ? mid : nkt;
+    } else if ((u.qt & 1u) == 0) {
+      return;
+    }
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -246,21 +262,21 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   // then the K_nope / V rows, then Q, so the K_rope loads wait for the page ids
   // only; the sign of a negative scale is applied to Q once it has arrived.
   uint32_t pg_next[2] = {0u, 0u};
-  if (nkt > 0) {
-    const uint32_t pg0[2] = {page_of(0, 0), page_of(0, 1)};
-    pg_next[0] = page_of(1, 0);
-    pg_next[1] = page_of(1, 1);
+  if (kt_hi > kt_lo) {
+    const uint32_t pg0[2] = {page_of(kt_lo, 0), page_of(kt_lo, 1)};
+    pg_next[0] = page_of(kt_lo + 1, 0);
+    pg_next[1] = page_of(kt_lo + 1, 1);
     // all four waves start their first tile together.  (Measured on the single
     // 16K-token sequence: how far apart the workgroups' K/V streams run, and so
     // the L2 hit rate, depends on this start-up; this form gives 7x algorithmic
     // HBM traffic where others gave up to 19x.)
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    issue_kv(0, 0);
+    issue_kv(kt_lo, kt_lo & 1);
     __builtin_amdgcn_sched_barrier(0);
     load_q();
     __builtin_amdgcn_sched_barrier(0);
-    issue_rope(0, 0, pg0);
+    issue_rope(kt_lo, kt_lo & 1, pg0);
   } else {
     // With no key to attend to, Q is never read (the epilogue writes 0 or passes
     // an earlier partial through).  The load stays: without this branch the
@@ -269,17 +285,17 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     load_q();
   }
 
-  for (int32_t kt = 0; kt < nkt; ++kt) {
+  for (int32_t kt = kt_lo; kt < kt_hi; ++kt) {
     const int stage = kt & 1;
     // publish tile kt (every wave's loads done) and retire stage (kt+1)&1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt == 0 && a.scale < 0.f) {
+    if (kt == kt_lo && a.scale < 0.f) {
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks)
         qop[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(i32x4, qop[ks]) ^ (int)0x80008000);
     }
-    if (kt + 1 < nkt) {
+    if (kt + 1 < kt_hi) {
       issue_kv(kt + 1, stage ^ 1);
       issue_rope(kt + 1, stage ^ 1, pg_next);
       pg_next[0] = page_of(kt + 2, 0);
@@ -390,21 +406,34 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   if (my_i < (int32_t)n) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    store_output_row<PLAIN>(row_target(a, row_first, row_last), (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
+    if (KVSPLIT && part)
+      store_output_row<false>(kv_split_target(a, (u.qt & 1u) ^ 1u), (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
+    else
+      store_output_row<PLAIN>(row_target(a, row_first, row_last), (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
   }
 }
 
 hipError_t launch_prefill_bf16(PrefillArgs a, uint32_t q_max, hipStream_t stream) {
   a.qtiles = (q_max + BM - 1) / BM;
-  const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles;
+  const bool kv_split = a.split_keys != 0;
+  const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles * (kv_split ? 2u : 1u);
   const uint64_t grid = (units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   const bool plain = !a.out_fp32 && !a.lse && !a.prev_out && !a.row_mode;
+  if (kv_split) {
+    // full query, no row mode, no earlier partial (the entry point checks)
+    auto kernel = a.causal ? (plain ? prefill_bf16_kernel<true, true, false, true> : prefill_bf16_kernel<true, false, false, true>)
+                           : (plain ? prefill_bf16_kernel<false, true, false, true> : prefill_bf16_kernel<false, false, false, true>);
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_kv_split_merge(a, stream);
+  }
   auto kernel = a.q_split
-      ? (a.causal ? (plain ? prefill_bf16_kernel<true, true, true> : prefill_bf16_kernel<true, false, true>)
-                  : (plain ? prefill_bf16_kernel<false, true, true> : prefill_bf16_kernel<false, false, true>))
-      : (a.causal ? (plain ? prefill_bf16_kernel<true, true, false> : prefill_bf16_kernel<true, false, false>)
-                  : (plain ? prefill_bf16_kernel<false, true, false> : prefill_bf16_kernel<false, false, false>));
+      ? (a.causal ? (plain ? prefill_bf16_kernel<true, true, true, false> : prefill_bf16_kernel<true, false, true, false>)
+                  : (plain ? prefill_bf16_kernel<false, true, true, false> : prefill_bf16_kernel<false, false, true, false>))
+      : (a.causal ? (plain ? prefill_bf16_kernel<true, true, false, false> : prefill_bf16_kernel<true, false, false, false>)
+                  : (plain ? prefill_bf16_kernel<false, true, false, false> : prefill_bf16_kernel<false, false, false, false>));
   hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }

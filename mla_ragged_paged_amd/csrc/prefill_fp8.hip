@@ -80,7 +80,10 @@ __device__ __forceinline__ i32x2 e4m3x4_to_bf16x4(int x) {
 //      K_rope e4m3 from the paged cache, converted exactly to bf16 for the rope
 //      product, which runs on the bf16 MFMA;
 //   2  split as 1, K_rope bf16 (paged bf16 cache or contiguous rows laid out like K).
-template <bool CAUSAL, bool PLAIN, int QM>
+// KVSPLIT: the grid holds two units per query tile, and a tile that
+// kv_split_tile selects is computed as two halves of its key tiles into the
+// workspace (QM 0 only).
+template <bool CAUSAL, bool PLAIN, int QM, bool KVSPLIT>
 __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   // K_rope rows of a stage: 64 bytes (e4m3) or 128 bytes (bf16)
   constexpr int KR_ROW = QM == 2 ? 128 : 64;
@@ -89,11 +92,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
 
-  // ---- work unit (XCD- and shader-engine-aware order, longest tiles first)
+  // ---- work unit (XCD- and shader-engine-aware order, longest tiles first).
+  // Key split: virtual tile 2qt + 1 (launched first) takes tile qt's first half,
+  // or the whole tile when it is not split; 2qt takes the second half.
   const uint32_t bid = blockIdx.x;
   WorkUnit u;
-  if (!decode_unit(bid, a.heads, a.batch, a.qtiles, u)) return;
-  const uint32_t h = u.h, b = u.b, qt = u.qt;
+  if (!decode_unit(bid, a.heads, a.batch, KVSPLIT ? 2u * a.qtiles : a.qtiles, u)) return;
+  const uint32_t h = u.h, b = u.b, qt = KVSPLIT ? u.qt >> 1 : u.qt;
   const uint32_t t0 = a.valid_length[b];
   const uint32_t n = a.valid_length[b + 1] - t0;
   const uint32_t i0 = qt * BM;
@@ -119,6 +124,18 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   constexpr bool causal = CAUSAL;
   const int32_t jend = causal ? max(0, min(p + i_last - c0 + 1, len)) : len;
   const int32_t nkt = (jend + BN - 1) / BN;
+  int32_t kt_lo = 0, kt_hi = nkt;                     // this unit's key tiles
+  bool part = false;                                  // key split: writes a partial
+  if constexpr (KVSPLIT) {
+    part = kv_split_tile(jend, a.split_keys);
+    const int32_t mid = (nkt + 1) >> 1;
+    if (part) {
+      kt_lo = (u.qt & 1u) ? 0 : mid;
+      kt_hi = (u.qt & 1u) ? mid : nkt;
+    } else if ((u.qt & 1u) == 0) {
+      return;
+    }
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -276,21 +293,21 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   // ---- prologue, ordered for the first tile's critical path: page ids first,
   // then the K_nope / V rows, then Q, so the K_rope loads wait for the page ids only
   uint32_t pg_next[2] = {0u, 0u};
-  if (nkt > 0) {
+  if (kt_hi > kt_lo) {
     uint32_t pg0[2] = {0u, 0u};
 #pragma unroll
     for (int u = 0; u < KRL; ++u) {
-      pg0[u] = page_of(0, u);
-      pg_next[u] = page_of(1, u);
+      pg0[u] = page_of(kt_lo, u);
+      pg_next[u] = page_of(kt_lo + 1, u);
     }
     // all four waves start their first tile together
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    issue_kv(0, stage0);
+    issue_kv(kt_lo, stage0);
     __builtin_amdgcn_sched_barrier(0);
     load_q();
     __builtin_amdgcn_sched_barrier(0);
-    issue_rope(0, stage0, pg0);
+    issue_rope(kt_lo, stage0, pg0);
   }
   // with no key to attend to, Q is never read (the epilogue writes 0, or passes
   // an earlier partial through)
@@ -298,7 +315,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   auto step = [&](int32_t kt, const uint8_t* st, uint8_t* next) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt == 0 && a.scale < 0.f) {
+    if (kt == kt_lo && a.scale < 0.f) {
 #pragma unroll
       for (int ks = 0; ks < QKS; ++ks) qop[ks] ^= (int)0x80808080;
       if constexpr (QM != 0) {
@@ -307,7 +324,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
           qr[r] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(i32x4, qr[r]) ^ (int)0x80008000);
       }
     }
-    if (kt + 1 < nkt) {
+    if (kt + 1 < kt_hi) {
       issue_kv(kt + 1, next);
       issue_rope(kt + 1, next, pg_next);
 #pragma unroll
@@ -451,9 +468,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       }
     }
   };
-  for (int32_t kt = 0; kt < nkt; kt += 2) {
+  for (int32_t kt = kt_lo; kt < kt_hi; kt += 2) {
     step(kt, stage0, stage1);
-    if (kt + 1 < nkt) step(kt + 1, stage1, stage0);
+    if (kt + 1 < kt_hi) step(kt + 1, stage1, stage0);
   }
 
   // ---- epilogue: row sums of both halves, normalise (applying s_v), store the
@@ -462,20 +479,33 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   if (my_i < (int32_t)n) {
     const float inv = l_tot > 0.f ? s_v / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    store_output_row<PLAIN>(row_target(a, row_first, row_last), (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
+    if (KVSPLIT && part)
+      store_output_row<false>(kv_split_target(a, (u.qt & 1u) ^ 1u), (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
+    else
+      store_output_row<PLAIN>(row_target(a, row_first, row_last), (size_t)(t0 + my_i) * H + h, hf, o, inv, lse2);
   }
 }
 
 hipError_t launch_prefill_fp8(PrefillArgs a, uint32_t q_max, hipStream_t stream) {
   a.qtiles = (q_max + BM - 1) / BM;
-  const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles;
+  const bool kv_split = a.split_keys != 0;
+  const uint64_t units = (uint64_t)a.heads * a.batch * a.qtiles * (kv_split ? 2u : 1u);
   const uint64_t grid = (units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   const bool plain = !a.out_fp32 && !a.lse && !a.prev_out && !a.row_mode;
+  if (kv_split) {
+    // full query, no row mode, no earlier partial (the entry point checks)
+    auto kernel = a.causal ? (plain ? prefill_fp8_kernel<true, true, 0, true> : prefill_fp8_kernel<true, false, 0, true>)
+                           : (plain ? prefill_fp8_kernel<false, true, 0, true> : prefill_fp8_kernel<false, false, 0, true>);
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NT), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_kv_split_merge(a, stream);
+  }
   auto pick = [&](auto qm) {
     constexpr int QM = decltype(qm)::value;
-    return a.causal ? (plain ? prefill_fp8_kernel<true, true, QM> : prefill_fp8_kernel<true, false, QM>)
-                    : (plain ? prefill_fp8_kernel<false, true, QM> : prefill_fp8_kernel<false, false, QM>);
+    return a.causal ? (plain ? prefill_fp8_kernel<true, true, QM, false> : prefill_fp8_kernel<true, false, QM, false>)
+                    : (plain ? prefill_fp8_kernel<false, true, QM, false> : prefill_fp8_kernel<false, false, QM, false>);
   };
   auto kernel = a.q_split == 0 ? pick(std::integral_constant<int, 0>{})
                                : a.q_split == 1 ? pick(std::integral_constant<int, 1>{})

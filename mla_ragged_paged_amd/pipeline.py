@@ -18,9 +18,38 @@ import torch
 from . import _binding as B
 from .workloads import Workload
 
+# Workgroup slots of the attention grid: 256 CUs x 2 resident workgroups.
+ATTENTION_SLOTS = 512
+QUERY_TILE = 128
+
 
 def _u32(a, device):
     return torch.from_numpy(a.astype("int64")).to(torch.int32).to(device)
+
+
+def balanced_split_keys(new_lengths, cache_lengths, heads: int, causal: bool = True,
+                        slots: int = ATTENTION_SLOTS) -> int:
+    """split_keys for mla_prefill_ragged_kvsplit from the host-side lengths of a batch.
+
+    The attention grid has one workgroup per (head, sequence, 128-query tile).
+    When it holds fewer of them than the chip has workgroup slots, every tile
+    runs at once and the launch lasts as long as its costliest tile: splitting
+    the tiles that see more than half the most keys any tile sees halves that.
+    With at least as many tiles as slots the kernel runs at full occupancy
+    until its tail and the split only adds the merge pass (measured on
+    DeepSeek-V3-shaped batches at 8, 16 and 32 heads): 0, no split.
+    """
+    tiles = 0
+    most = 0
+    for n, p in zip((int(x) for x in new_lengths), (int(x) for x in cache_lengths)):
+        for i0 in range(0, n, QUERY_TILE):
+            tiles += 1
+            keys = p + min(n, i0 + QUERY_TILE) if causal else p + n
+            most = max(most, keys)
+    if heads * tiles >= slots:
+        return 0
+    threshold = max(128, -(-most // 2))
+    return threshold if most > threshold else 0
 
 
 class PrefillStep:
@@ -32,10 +61,13 @@ class PrefillStep:
     ([H*256, latent_dim] bf16) K_nope / V are not the workload's tensors but are
     decompressed per buffer row from the latent cache (columns
     ``latent_col`` .. +latent_dim), which replaces the gather step.
+    ``split_keys`` > 0 (one buffer row only) runs the attention through
+    mla_prefill_ragged_kvsplit with that threshold and a workspace allocated
+    here; "auto" takes balanced_split_keys of the workload.
     """
 
     def __init__(self, w: Workload, device="cuda", cap: int | None = None, gather_cols=None, mask="causal",
-                 kv_b_weight=None, latent_col=0):
+                 kv_b_weight=None, latent_col=0, split_keys=0):
         self.w = w
         self.mask = mask
         self.device = torch.device(device)
@@ -77,6 +109,15 @@ class PrefillStep:
         if self.rows > 1:
             self.acc = torch.zeros((w.total_q, w.heads, 128), dtype=torch.float32, device=dev)
             self.lse = torch.zeros((w.total_q, w.heads), dtype=torch.float32, device=dev)
+        if split_keys == "auto":
+            split_keys = balanced_split_keys(w.n, w.p, w.heads, causal=mask == "causal")
+        self.split_keys = int(split_keys)
+        self.workspace = None
+        if self.split_keys:
+            if self.rows > 1:
+                raise ValueError("split_keys needs a single buffer row")
+            nbytes = B.mla_prefill_kvsplit_workspace_bytes(w.total_q, w.heads)
+            self.workspace = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=dev)
 
     def row_buffers(self, row: int):
         """K_nope / V of plan row ``row``.  The workload's buffers hold every
@@ -106,6 +147,15 @@ class PrefillStep:
         """Attention over plan row ``row``; k_nope / v default to the workload's buffer (one-row layout)."""
         co = self.cache_offsets[row] if isinstance(cache_offsets, str) else cache_offsets
         sc = self.scales or {}
+        if self.split_keys:
+            B.mla_prefill_ragged_kvsplit(self.out if out is None else out, self.q,
+                                         self.k_nope if k_nope is None else k_nope, self.v if v is None else v,
+                                         self.kv, self.w.spec.layer_idx, self.input_row_offsets,
+                                         self.buffer_row_offsets[row], co, self.w.softmax_scale, self.split_keys,
+                                         self.workspace, q_scale=sc.get("q"), k_nope_scale=sc.get("k_nope"),
+                                         v_scale=sc.get("v"), q_max_seq_len=self.w.max_q, stream=stream,
+                                         mask=self.mask)
+            return
         B.mla_prefill_ragged(self.out if out is None else out, self.q, self.k_nope if k_nope is None else k_nope,
                              self.v if v is None else v, self.kv, self.w.spec.layer_idx, self.input_row_offsets,
                              self.buffer_row_offsets[row], co, self.w.softmax_scale, sc.get("q"),

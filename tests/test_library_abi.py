@@ -28,9 +28,11 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_last_hip_error", "mla_prefill_latent_up", "mla_prefill_merge",
-                                    "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_lse",
-                                    "mla_prefill_ragged_row", "mla_prefill_ragged_split", "mla_status_string"]
+    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_kvsplit_workspace_bytes",
+                                    "mla_prefill_last_hip_error", "mla_prefill_latent_up", "mla_prefill_merge",
+                                    "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_kvsplit",
+                                    "mla_prefill_ragged_lse", "mla_prefill_ragged_row", "mla_prefill_ragged_split",
+                                    "mla_status_string"]
 
 
 def test_binding_exposes_every_entry_point():
@@ -134,6 +136,22 @@ def test_lse_and_merge_validation_without_gpu():
     s.dtype = 1
     assert lib.mla_prefill_ragged_split(*split_args(rows=None)) == 3          # bf16 q_nope with an e4m3 cache
     s.dtype = 0
+
+    # key split: 4 tokens x 2 heads need 4 * 2 * (2 * 128 + 2) * 4 bytes of workspace
+    lib.mla_prefill_kvsplit_workspace_bytes.restype = ctypes.c_uint64
+    assert lib.mla_prefill_kvsplit_workspace_bytes(4, 2) == 8256
+    assert lib.mla_prefill_kvsplit_workspace_bytes(0, 16) == 0
+
+    def kvs_args(**kw):
+        return [dummy, 0, None, dummy, 0, dummy, dummy, ref, 0, dummy, dummy, None, 1, 4, 2, kw.get("qd", 192), 128,
+                0, ctypes.c_float(0.07), None, None, None, 0, kw.get("sk", 256), kw.get("ws", dummy),
+                ctypes.c_uint64(kw.get("wb", 8256)), None]
+    assert lib.mla_prefill_ragged_kvsplit(*kvs_args(ws=None)) == 1          # split without a workspace
+    assert lib.mla_prefill_ragged_kvsplit(*kvs_args(sk=64)) == 2            # split_keys below 128
+    assert lib.mla_prefill_ragged_kvsplit(*kvs_args(sk=1)) == 2
+    assert lib.mla_prefill_ragged_kvsplit(*kvs_args(wb=8255)) == 2          # workspace one byte short
+    assert lib.mla_prefill_ragged_kvsplit(*kvs_args(ws=ctypes.c_void_p(24))) == 2   # misaligned workspace
+    assert lib.mla_prefill_ragged_kvsplit(*kvs_args(qd=128)) == 4           # split query is not offered
 
     def lat_args(**kw):
         return [ref, 0, kw.get("b", 1), dummy, dummy, kw.get("col", 0), kw.get("dim", 64), kw.get("w", dummy), 2,
