@@ -28,6 +28,10 @@
  *                       key range of long query tiles split over two workgroups
  *                       and merged (for grids with few tiles, e.g. few heads).
  *
+ *   mla_prefill_check   tests on the device the preconditions the calls document
+ *                       but do not check (offsets, positions, page ids);
+ *                       mla_prefill_set_debug makes every call run it first.
+ *
  * When the plan cuts the contexts over several buffer rows, each row's
  * attention covers part of a sequence's keys:
  *
@@ -46,12 +50,17 @@
  *     `stream` (a hipStream_t passed as void*; NULL = the null stream); it never
  *     synchronises.  The caller owns all memory and keeps it alive and unchanged
  *     until the enqueued work has finished.  The library allocates no device
- *     memory and keeps no state beyond its loaded code objects; calls are
+ *     memory and keeps no state beyond its loaded code objects (debug mode
+ *     aside: its on/off setting and one 4-byte flag per GPU); calls are
  *     thread-safe.  Outputs must not alias inputs, except where a call says so.
  *   - Host-checkable errors are returned before anything is enqueued (nothing
  *     is written).  Properties of device data (monotone offsets, in-range page
  *     ids, lengths) are preconditions that are NOT checked: violating them is
- *     undefined behaviour.  MLA_ERR_HIP reports a failed launch
+ *     undefined behaviour; mla_prefill_check tests them on the device, and in
+ *     debug mode (mla_prefill_set_debug, or MLA_PREFILL_DEBUG=1 in the
+ *     environment when the library loads) every call runs that check first,
+ *     synchronises and returns MLA_ERR_PRECONDITION instead of launching on
+ *     violating data.  MLA_ERR_HIP reports a failed launch
  *     (hipGetLastError after the enqueue); mla_prefill_last_hip_error() then
  *     returns the HIP error code.
  *   - batch_size == 0 (or total_q_tokens == 0 for the attention) is a valid no-op.
@@ -72,7 +81,9 @@ typedef enum {
   MLA_ERR_UNSUPPORTED_DTYPE = 3, /* dtype combination not offered */
   MLA_ERR_UNSUPPORTED_DIMS = 4,  /* q_depth != 192 or depth != 128 */
   MLA_ERR_UNSUPPORTED_MASK = 5,  /* mask kind not offered */
-  MLA_ERR_HIP = 6                /* the HIP runtime reported an error on enqueue */
+  MLA_ERR_HIP = 6,               /* the HIP runtime reported an error on enqueue */
+  MLA_ERR_PRECONDITION = 7       /* debug mode only: the device data violate a documented
+                                    precondition (see mla_prefill_check); nothing was launched */
 } mla_status_t;
 
 /* Element types ("flare_mla_prefill", Parameters: q is bfloat16 or float8_e4m3fn;
@@ -462,6 +473,64 @@ mla_status_t mla_prefill_ragged_row(void* output, mla_dtype_t output_dtype, floa
 mla_status_t mla_prefill_merge(void* output, mla_dtype_t output_dtype, float* lse, const float* o_a,
                                const float* lse_a, const float* o_b, const float* lse_b,
                                uint32_t total_q_tokens, uint32_t num_heads, uint32_t depth, void* stream);
+
+/*
+ * mla_prefill_check -- tests on the device the preconditions of the plan,
+ * gather, attention and decompression calls that the host cannot see (their
+ * documented "not checked" device data: page "generic_flare_mla_prefill_ragged_paged_plan",
+ * Args, and page "flare_mla_prefill", Args, for the meaning of each array), and
+ * ORs the bits of every violated one into *violations.  It reads the arrays
+ * only inside their documented extents (page-table reads are clamped to the
+ * sequence's row of max_pages_per_seq entries) and never uses a value it
+ * checks as an address, so it is safe on any data.
+ *
+ *   kv              [host] cache descriptor: cache_lengths (device [B]) is
+ *                   required; page_table may be NULL (no paged reads to check,
+ *                   e.g. contiguous K_rope rows), else page_size,
+ *                   max_pages_per_seq and num_pages must be > 0.
+ *   valid_length    device [B+1] new-token offsets, or NULL (not checked).
+ *   total_q_tokens  checked against valid_length[B] unless it is 0xFFFFFFFF.
+ *   q_max_seq_len   0, or a bound every n_b must meet.
+ *   row_offsets     device [B+1] one buffer row's offsets (cache_row_offsets /
+ *                   buffer_row_offsets[r]), or NULL: the call then reads
+ *                   positions [0, p_b + n_b) of every sequence (needs valid_length).
+ *   row_positions   device [B] that row's first cache positions
+ *                   (cache_offsets[r]), or NULL (0).
+ *   row_capacity    0, or a bound row_offsets[B] must meet (buffer_token_size,
+ *                   or the rows of K_nope / V).
+ *   violations      device int32, ORed with:
+ *     MLA_VIOLATION_Q_OFFSETS    valid_length[0] != 0, a decreasing step,
+ *                                valid_length[B] != total_q_tokens, or n_b > q_max_seq_len;
+ *     MLA_VIOLATION_ROW_OFFSETS  a decreasing step of row_offsets, or
+ *                                row_offsets[B] > row_capacity;
+ *     MLA_VIOLATION_POSITIONS    a row's positions reach past p_b + n_b (with
+ *                                valid_length) or past max_pages_per_seq * page_size;
+ *     MLA_VIOLATION_PAGE_IDS     a page id behind a position the call reads is
+ *                                >= num_pages.
+ *                   The caller zeroes it; the call never clears bits.
+ * Enqueues one small kernel (one wave per sequence); no synchronisation, no
+ * allocation.  Errors: NULL_ARG, BAD_SHAPE (batch_size > MLA_MAX_BATCH, a
+ * zero page size / page count with a page table), HIP.
+ */
+#define MLA_VIOLATION_Q_OFFSETS 1
+#define MLA_VIOLATION_ROW_OFFSETS 2
+#define MLA_VIOLATION_POSITIONS 4
+#define MLA_VIOLATION_PAGE_IDS 8
+mla_status_t mla_prefill_check(const mla_paged_cache_t* kv, const uint32_t* valid_length, uint32_t batch_size,
+                               uint32_t total_q_tokens, uint32_t q_max_seq_len, const uint32_t* row_offsets,
+                               const uint32_t* row_positions, uint32_t row_capacity, int32_t* violations,
+                               void* stream);
+
+/* Debug mode on (nonzero) or off, for every thread of the process; returns the
+ * previous setting.  In debug mode each plan, gather, attention and
+ * decompression call first runs mla_prefill_check on its own arguments (with
+ * the capacity, q_max_seq_len and token count it was given), waits for it
+ * (hipStreamSynchronize on the call's stream, so a call in debug mode cannot
+ * be captured into a graph), and returns MLA_ERR_PRECONDITION without
+ * launching anything when a bit is set.  Debug mode keeps one 4-byte device
+ * flag per GPU, allocated on its first use there.  It starts on when the
+ * environment variable MLA_PREFILL_DEBUG is "1" as the library loads. */
+int mla_prefill_set_debug(int on);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* mla_status_string(mla_status_t status);

@@ -8,14 +8,20 @@ been built; there is no fallback.
 """
 from ._binding import (  # noqa: F401
     MLA_BF16,
+    MLA_ERR_PRECONDITION,
     MLA_FP8_E4M3FN,
     MLA_FP32,
     MLA_MASK_CAUSAL,
     MLA_MASK_NULL,
     MLA_MAX_BATCH,
+    MLA_VIOLATION_PAGE_IDS,
+    MLA_VIOLATION_POSITIONS,
+    MLA_VIOLATION_Q_OFFSETS,
+    MLA_VIOLATION_ROW_OFFSETS,
     MlaError,
     PagedCache,
     library_path,
+    mla_prefill_check,
     mla_prefill_gather,
     mla_prefill_kvsplit_workspace_bytes,
     mla_prefill_last_hip_error,
@@ -27,5 +33,6 @@ from ._binding import (  # noqa: F401
     mla_prefill_ragged_lse,
     mla_prefill_ragged_row,
     mla_prefill_ragged_split,
+    mla_prefill_set_debug,
     mla_status_string,
 )

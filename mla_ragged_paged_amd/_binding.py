@@ -24,9 +24,15 @@ MLA_MASK_CAUSAL = 0
 MLA_MASK_NULL = 1
 _MASKS = {"causal": MLA_MASK_CAUSAL, "null": MLA_MASK_NULL}
 MLA_MAX_BATCH = 8192
+MLA_ERR_PRECONDITION = 7
+MLA_VIOLATION_Q_OFFSETS = 1
+MLA_VIOLATION_ROW_OFFSETS = 2
+MLA_VIOLATION_POSITIONS = 4
+MLA_VIOLATION_PAGE_IDS = 8
 
 _STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_SHAPE", 3: "MLA_ERR_UNSUPPORTED_DTYPE",
-                 4: "MLA_ERR_UNSUPPORTED_DIMS", 5: "MLA_ERR_UNSUPPORTED_MASK", 6: "MLA_ERR_HIP"}
+                 4: "MLA_ERR_UNSUPPORTED_DIMS", 5: "MLA_ERR_UNSUPPORTED_MASK", 6: "MLA_ERR_HIP",
+                 7: "MLA_ERR_PRECONDITION"}
 
 
 class MlaError(RuntimeError):
@@ -83,6 +89,10 @@ def _load():
     lib.mla_prefill_latent_up.restype = i32
     lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
     lib.mla_prefill_merge.restype = i32
+    lib.mla_prefill_check.argtypes = [cp, vp, u32, u32, u32, vp, vp, u32, vp, vp]
+    lib.mla_prefill_check.restype = i32
+    lib.mla_prefill_set_debug.argtypes = [i32]
+    lib.mla_prefill_set_debug.restype = i32
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_prefill_last_hip_error.argtypes = []
@@ -252,6 +262,26 @@ def mla_prefill_ragged_lse(output, lse, q, k_nope, v, k_rope: PagedCache, layer_
                                        k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
                                        _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
            "mla_prefill_ragged_lse")
+
+
+def mla_prefill_check(kv: PagedCache, violations, valid_length=None, total_q_tokens=None, q_max_seq_len=0,
+                      row_offsets=None, row_positions=None, row_capacity=0, stream=None):
+    """Device-side check of a call's device data: ORs MLA_VIOLATION_* bits into ``violations``
+    (a one-element int32 device tensor the caller zeroes).  ``total_q_tokens`` None: not checked."""
+    if violations.dtype != torch.int32 or violations.numel() < 1:
+        raise TypeError("violations must be an int32 tensor")
+    batch = (valid_length if valid_length is not None else row_offsets).shape[0] - 1
+    s = kv.as_struct()
+    T = 0xFFFFFFFF if total_q_tokens is None else int(total_q_tokens)
+    _check(_lib.mla_prefill_check(ctypes.byref(s), _idx(valid_length, "valid_length"), batch, T, int(q_max_seq_len),
+                                  _idx(row_offsets, "row_offsets"), _idx(row_positions, "row_positions"),
+                                  int(row_capacity), _ptr(violations), _stream(stream)),
+           "mla_prefill_check")
+
+
+def mla_prefill_set_debug(on: bool) -> bool:
+    """Debug mode on or off (every call checks its device data first); returns the previous setting."""
+    return bool(_lib.mla_prefill_set_debug(1 if on else 0))
 
 
 def mla_prefill_kvsplit_workspace_bytes(total_q_tokens: int, num_heads: int) -> int:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_prefill.so")
-SOURCES = ["api.hip", "plan_gather.hip", "prefill_bf16.hip", "prefill_fp8.hip", "merge.hip", "latent_up.hip"]
+SOURCES = ["api.hip", "plan_gather.hip", "prefill_bf16.hip", "prefill_fp8.hip", "merge.hip", "latent_up.hip", "check.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

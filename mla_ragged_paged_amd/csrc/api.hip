@@ -4,11 +4,30 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
 #include "kernels.h"
+
+static_assert(mla::CHECK_Q_OFFSETS == MLA_VIOLATION_Q_OFFSETS && mla::CHECK_ROW_OFFSETS == MLA_VIOLATION_ROW_OFFSETS &&
+                  mla::CHECK_POSITIONS == MLA_VIOLATION_POSITIONS && mla::CHECK_PAGE_IDS == MLA_VIOLATION_PAGE_IDS,
+              "violation bits");
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// ---- debug mode: every call checks its device data first (mla_prefill_set_debug)
+int debug_from_env() {
+  const char* e = std::getenv("MLA_PREFILL_DEBUG");
+  return e && std::strcmp(e, "1") == 0 ? 1 : 0;
+}
+std::atomic<int> g_debug{debug_from_env()};
+std::mutex g_debug_mu;                 // one check at a time: the flag of a GPU is shared
+constexpr int MAX_DEVICES = 64;
+int32_t* g_debug_flag[MAX_DEVICES] = {};
 
 mla_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return MLA_OK;
@@ -30,6 +49,47 @@ mla_status_t check_cache(const mla_paged_cache_t* kv, uint32_t layer_idx) {
   return MLA_OK;
 }
 
+// Runs the device-side check of a call's arguments when debug mode is on: the
+// check kernel on the call's stream, then a wait for its flag.  No launch and
+// no wait when debug mode is off.
+mla_status_t debug_check(mla::CheckArgs c, void* stream) {
+  if (g_debug.load(std::memory_order_relaxed) == 0 || c.batch == 0) return MLA_OK;
+  std::lock_guard<std::mutex> lock(g_debug_mu);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= MAX_DEVICES) return MLA_ERR_BAD_SHAPE;
+  if (!g_debug_flag[dev]) {
+    e = hipMalloc(reinterpret_cast<void**>(&g_debug_flag[dev]), sizeof(int32_t));
+    if (e != hipSuccess) return hip_status(e);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  static const int32_t zero = 0;
+  int32_t found = 0;
+  c.violations = g_debug_flag[dev];
+  e = hipMemcpyAsync(c.violations, &zero, sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = mla::launch_check(c, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&found, c.violations, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  return found ? MLA_ERR_PRECONDITION : MLA_OK;
+}
+
+// Check arguments with the paged-cache fields of a descriptor (page table
+// optional) and nothing else set.
+mla::CheckArgs check_args(const mla_paged_cache_t* kv, uint32_t batch) {
+  mla::CheckArgs c{};
+  c.batch = batch;
+  c.cache_lengths = kv->cache_lengths;
+  if (kv->page_table && kv->page_size && kv->max_pages_per_seq && kv->num_pages) {
+    c.page_table = kv->page_table;
+    c.max_pages = kv->max_pages_per_seq;
+    c.page_size = kv->page_size;
+    c.num_pages = kv->num_pages;
+  }
+  return c;
+}
+
 const uint8_t* layer_base(const mla_paged_cache_t* kv, uint32_t layer_idx) {
   return static_cast<const uint8_t*>(kv->data) +
          (size_t)layer_idx * kv->num_pages * kv->page_size * kv->row_width * dtype_bytes(kv->dtype);
@@ -48,11 +108,37 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_UNSUPPORTED_DIMS: return "MLA_ERR_UNSUPPORTED_DIMS: q_depth must be 192 and depth 128";
     case MLA_ERR_UNSUPPORTED_MASK: return "MLA_ERR_UNSUPPORTED_MASK: the mask is neither causal nor null";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported an error";
+    case MLA_ERR_PRECONDITION:
+      return "MLA_ERR_PRECONDITION: the device data violate a documented precondition (debug mode)";
   }
   return "unknown mla_status_t";
 }
 
 int mla_prefill_last_hip_error(void) { return g_last_hip_error; }
+
+int mla_prefill_set_debug(int on) { return g_debug.exchange(on ? 1 : 0); }
+
+mla_status_t mla_prefill_check(const mla_paged_cache_t* kv, const uint32_t* valid_length, uint32_t batch_size,
+                               uint32_t total_q_tokens, uint32_t q_max_seq_len, const uint32_t* row_offsets,
+                               const uint32_t* row_positions, uint32_t row_capacity, int32_t* violations,
+                               void* stream) {
+  if (!kv || !kv->cache_lengths || !violations) return MLA_ERR_NULL_ARG;
+  if (!valid_length && !row_offsets) return MLA_ERR_NULL_ARG;
+  if (batch_size > MLA_MAX_BATCH) return MLA_ERR_BAD_SHAPE;
+  if (kv->page_table && (kv->page_size == 0 || kv->max_pages_per_seq == 0 || kv->num_pages == 0))
+    return MLA_ERR_BAD_SHAPE;
+  if (batch_size == 0) return MLA_OK;
+  mla::CheckArgs c = check_args(kv, batch_size);
+  c.valid_length = valid_length;
+  c.tokens = total_q_tokens;
+  c.tokens_known = total_q_tokens != 0xFFFFFFFFu ? 1u : 0u;
+  c.q_max = q_max_seq_len;
+  c.row_offsets = row_offsets;
+  c.row_positions = row_positions;
+  c.row_capacity = row_capacity;
+  c.violations = violations;
+  return hip_status(mla::launch_check(c, static_cast<hipStream_t>(stream)));
+}
 
 mla_status_t mla_prefill_plan(const uint32_t* input_row_offsets, uint32_t batch_size, const mla_paged_cache_t* kv,
                               uint32_t layer_idx, uint32_t buffer_token_size, uint32_t num_buffer_rows,
@@ -63,6 +149,13 @@ mla_status_t mla_prefill_plan(const uint32_t* input_row_offsets, uint32_t batch_
   if (kv->num_layers == 0 || layer_idx >= kv->num_layers) return MLA_ERR_BAD_SHAPE;
   if (buffer_token_size == 0 || buffer_token_size > 0x7FFFFFFFu || num_buffer_rows == 0) return MLA_ERR_BAD_SHAPE;
   if (batch_size > MLA_MAX_BATCH) return MLA_ERR_BAD_SHAPE;
+  {
+    // the whole batch: offsets, and the pages of every position a later gather reads
+    mla::CheckArgs c = check_args(kv, batch_size);
+    c.valid_length = input_row_offsets;
+    mla_status_t st = debug_check(c, stream);
+    if (st != MLA_OK) return st;
+  }
   mla::PlanArgs a{};
   a.input_row_offsets = input_row_offsets;
   a.cache_lengths = kv->cache_lengths;
@@ -87,6 +180,14 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
   if (batch_size > MLA_MAX_BATCH || col_count == 0 || (uint64_t)col_begin + col_count > kv->row_width ||
       buffer_token_size == 0)
     return MLA_ERR_BAD_SHAPE;
+  {
+    mla::CheckArgs c = check_args(kv, batch_size);
+    c.row_offsets = buffer_row_offsets_r;
+    c.row_positions = cache_offsets_r;
+    c.row_capacity = buffer_token_size;
+    st = debug_check(c, stream);
+    if (st != MLA_OK) return st;
+  }
   const size_t el = dtype_bytes(kv->dtype);
   mla::GatherArgs a{};
   a.cache = layer_base(kv, layer_idx);
@@ -202,6 +303,19 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
   const uint64_t units = (uint64_t)num_heads * batch_size * ((q_max + 127) / 128) * (kvs.split_keys ? 2u : 1u);
   if (units > 0x7FFFFFF0ull) return MLA_ERR_BAD_SHAPE;
 
+  {
+    // this row's keys (and, through the page table, their K_rope rows)
+    mla::CheckArgs c = check_args(k_rope, batch_size);
+    if (contig) c.page_table = nullptr;
+    c.valid_length = valid_length;
+    c.tokens = total_q_tokens;
+    c.tokens_known = 1u;
+    c.q_max = q_max_seq_len;
+    c.row_offsets = cache_row_offsets;
+    c.row_positions = cache_offsets;
+    mla_status_t st = debug_check(c, stream);
+    if (st != MLA_OK) return st;
+  }
   mla::PrefillArgs a{};
   a.out = output;
   a.lse = lse;
@@ -355,6 +469,14 @@ mla_status_t mla_prefill_latent_up(const mla_paged_cache_t* kv, uint32_t layer_i
   const uint64_t grid = ((uint64_t)buffer_token_size + 127) / 128 * 2 * num_heads;
   if (layer_bytes >= (1ull << 32) || 128ull * latent_dim * 2 >= (1ull << 31) || grid >= (1ull << 31))
     return MLA_ERR_BAD_SHAPE;
+  {
+    mla::CheckArgs c = check_args(kv, batch_size);
+    c.row_offsets = buffer_row_offsets_r;
+    c.row_positions = cache_offsets_r;
+    c.row_capacity = buffer_token_size;
+    st = debug_check(c, stream);
+    if (st != MLA_OK) return st;
+  }
   mla::LatentArgs a{};
   a.cache = layer_base(kv, layer_idx);
   a.page_table = kv->page_table;

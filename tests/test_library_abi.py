@@ -28,11 +28,11 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["mla_prefill_gather", "mla_prefill_kvsplit_workspace_bytes",
+    assert declared_functions() == ["mla_prefill_check", "mla_prefill_gather", "mla_prefill_kvsplit_workspace_bytes",
                                     "mla_prefill_last_hip_error", "mla_prefill_latent_up", "mla_prefill_merge",
                                     "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_kvsplit",
                                     "mla_prefill_ragged_lse", "mla_prefill_ragged_row", "mla_prefill_ragged_split",
-                                    "mla_status_string"]
+                                    "mla_prefill_set_debug", "mla_status_string"]
 
 
 def test_binding_exposes_every_entry_point():
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     lib.mla_status_string.restype = ctypes.c_char_p
-    for code in range(7):
+    for code in range(8):
         assert lib.mla_status_string(code).decode().startswith("MLA_")
     assert lib.mla_status_string(99) == b"unknown mla_status_t"
 
@@ -176,6 +176,39 @@ def test_lse_and_merge_validation_without_gpu():
     assert lib.mla_prefill_merge(*merge_args(oa=ctypes.c_void_p(20))) == 2
     assert lib.mla_prefill_merge(*merge_args(lb=ctypes.c_void_p(18))) == 2
     assert lib.mla_prefill_merge(*merge_args(t=0)) == 0                    # empty: a no-op
+
+
+def test_check_validation_and_debug_switch_without_gpu():
+    import subprocess
+    import sys
+    import mla_ragged_paged_amd._binding as b
+    lib = b._lib
+    dummy = ctypes.c_void_p(16)
+    s = b._Cache(data=16, dtype=0, num_layers=1, num_pages=1, page_size=16, row_width=64, rope_col=0,
+                 page_table=16, max_pages_per_seq=1, cache_lengths=16, scale=None)
+    ref = ctypes.byref(s)
+
+    def chk(kv=ref, vl=dummy, batch=1, rows=None, viol=dummy):
+        return lib.mla_prefill_check(kv, vl, batch, 4, 0, rows, None, 0, viol, None)
+    assert chk(kv=None) == 1
+    assert chk(viol=None) == 1
+    assert chk(vl=None, rows=None) == 1                  # nothing to check
+    assert chk(batch=8193) == 2
+    assert chk(batch=0) == 0                             # empty batch: a no-op
+    s.page_size = 0
+    assert chk() == 2                                    # a page table without a page size
+    s.page_size = 16
+    s.cache_lengths = None
+    assert chk() == 1
+    # the debug switch returns the previous setting; the environment sets it at load
+    prev = lib.mla_prefill_set_debug(1)
+    assert lib.mla_prefill_set_debug(prev) == 1
+    code = ("import ctypes; lib = ctypes.CDLL(%r); print(lib.mla_prefill_set_debug(0), lib.mla_prefill_set_debug(0))"
+            % LIB)
+    for env, want in (("1", "1 0"), ("0", "0 0"), ("", "0 0")):
+        out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                             env={**os.environ, "MLA_PREFILL_DEBUG": env}).stdout.split()
+        assert " ".join(out) == want, (env, out)
 
 
 def test_package_fails_loudly_without_the_library(tmp_path):
