@@ -9,6 +9,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "check.h"
 #include "kernels.h"
 
 static_assert(mla::CHECK_Q_OFFSETS == MLA_VIOLATION_Q_OFFSETS && mla::CHECK_ROW_OFFSETS == MLA_VIOLATION_ROW_OFFSETS &&

@@ -9,8 +9,7 @@
 // read (clamped to the sequence's page-table row, so the check itself reads
 // only inside its arrays) and compares them with the page count.  Values are
 // compared, never used as addresses.  Violations are ORed into one int32.
-#include "device_common.h"
-#include "kernels.h"
+#include "check.h"
 
 namespace mla {
 namespace {
