@@ -56,15 +56,23 @@ mla_status_t check_cache(const mla_paged_cache_t* kv, uint32_t layer_idx) {
 mla_status_t debug_check(mla::CheckArgs c, void* stream) {
   if (g_debug.load(std::memory_order_relaxed) == 0 || c.batch == 0) return MLA_OK;
   std::lock_guard<std::mutex> lock(g_debug_mu);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the flag lives on the stream's GPU (the current one for the null stream)
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(s, &dev);
   if (e != hipSuccess) return hip_status(e);
   if (dev < 0 || dev >= MAX_DEVICES) return MLA_ERR_BAD_SHAPE;
   if (!g_debug_flag[dev]) {
-    e = hipMalloc(reinterpret_cast<void**>(&g_debug_flag[dev]), sizeof(int32_t));
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&g_debug_flag[dev]), sizeof(int32_t));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
     if (e != hipSuccess) return hip_status(e);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   static const int32_t zero = 0;
   int32_t found = 0;
   c.violations = g_debug_flag[dev];

@@ -181,3 +181,40 @@ def test_one_gpu_share_of_the_heads_sampled(dtype):
     ref = oracle_rows(w, rows, bro[0], co[0])
     got = np.stack([out[t, h].cpu().numpy() for t, h in rows])
     assert report(got, ref, BAR[dtype], f"{w.spec.name}-kvsplit") <= BAR[dtype]
+
+
+@pytest.mark.parametrize("mask", ["causal", "null"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_kvsplit_per_buffer_row_then_merged(dtype, mask):
+    """A plan of four buffer rows, so rows start in the middle of sequences
+    (cache_offsets > 0) and some sequences have no key in a row: each row's
+    attention through the key split (split_keys 128) with its lse, the rows
+    combined with mla_prefill_merge, equals the attention over every key."""
+    w, ref = _case_reference(0, dtype, mask)
+    say(f"kv split per buffer row {dtype} {mask}: C={w.total_ctx}")
+    step = PrefillStep(w, "cuda", cap=1100, mask=mask)
+    step.plan()
+    check_plan(step, w)
+    assert step.rows == 4
+    sc = step.scales or {}
+    T, H = w.total_q, w.heads
+    ws = torch.full((m.mla_prefill_kvsplit_workspace_bytes(T, H) // 4,), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    acc = acc_lse = None
+    for r in range(step.rows):
+        kn, v = step.row_buffers(r)
+        o = torch.full((T, H, 128), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        m.mla_prefill_ragged_kvsplit(o, step.q, kn, v, step.kv, 0, step.input_row_offsets,
+                                     step.buffer_row_offsets[r], step.cache_offsets[r], w.softmax_scale, 128, ws,
+                                     lse=lse, q_scale=sc.get("q"), k_nope_scale=sc.get("k_nope"),
+                                     v_scale=sc.get("v"), q_max_seq_len=w.max_q, mask=mask)
+        if acc is None:
+            acc, acc_lse = o, lse
+        else:
+            merged = torch.empty_like(o)
+            merged_lse = torch.empty_like(lse)
+            m.mla_prefill_merge(merged, merged_lse, acc, acc_lse, o, lse)
+            acc, acc_lse = merged, merged_lse
+    torch.cuda.synchronize()
+    assert report(acc.cpu().numpy(), ref, BAR[dtype], f"kvsplit-rows-{dtype}-{mask}") <= BAR[dtype]
