@@ -37,6 +37,8 @@
 //        holds them; V is read in that same order.
 // Buffer descriptors are sized to the valid rows, so loads past the ragged
 // tail return zeros without branches.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -302,7 +304,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       pg_next[1] = page_of(kt + 2, 1);
     }
     const int32_t j0 = kt * BN;
-    if (wave_rows && (!causal || c0 + j0 <= wq_last)) {
+    // A wave whose last query comes before key 32 of the tile sees none of keys
+    // 32..63 (key block 1): its S^T block, softmax terms and P.V steps for them
+    // are skipped (they would add exact zeros), which saves their LDS reads.
+    const bool half_tile = causal && c0 + j0 + 32 > wq_last;
+    auto tile_body = [&](auto half_c) {
+      constexpr bool HALF = decltype(half_c)::value;
+      constexpr int KB = HALF ? 1 : 2;                 // key blocks of 32 this wave computes
       const uint8_t* st = lds + stage * STAGE;
       // S^T = K Q^T.  K fragments go through a three-deep register ring, read two
       // k-steps ahead of their MFMAs so LDS latency overlaps the MFMA chain; the
@@ -311,7 +319,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       bf16x8 kf[3][2];
       auto kread = [&](int ks, bf16x8 (&dst)[2]) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
           const uint32_t off = ks < 8 ? kn_rd[ks] + kb * 32 * 256 : kr_rd[ks - 8] + kb * 32 * 128;
           dst[kb] = *reinterpret_cast<const bf16x8*>(st + off);
         }
@@ -323,14 +331,14 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         if (ks + 2 < 12) kread(ks + 2, kf[(ks + 2) % 3]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(kf[ks % 3][kb], qop[ks], s[kb]);
+        for (int kb = 0; kb < KB; ++kb) s[kb] = mfma_bf16(kf[ks % 3][kb], qop[ks], s[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
       // s[kb][r] is key j0 + 32kb + 4hf + roff(r), roff(r) = 8(r/4) + r%4
       const bool full = (j0 + BN <= len) && (!causal || c0 + j0 + BN - 1 <= wq_first);
       if (!full) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
           const int32_t kbase = j0 + 32 * kb + 4 * hf;
           const int32_t lim = causal ? min(len - 1 - kbase, p + my_i - c0 - kbase) : len - 1 - kbase;
 #pragma unroll
@@ -354,7 +362,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       vread(0, vf[0]);
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = max_across_halves(mx);
@@ -369,7 +377,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       }
       uint32_t pw[16];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int x = 0; x < 8; ++x)
           pw[8 * kb + x] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * x], c, -mc)),
@@ -379,24 +387,30 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int x = 0; x < 16; x += 2) {
+        for (int x = 0; x < 8 * KB; x += 2) {
           ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x]), ones, ps0, false);
           ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x + 1]), ones, ps1, false);
         }
         l_run += ps0 + ps1;
       }
 
-      // O^T += V^T P^T, four 16-key steps; V fragments are read one step ahead
+      // O^T += V^T P^T, four (two) 16-key steps; V fragments are read one step ahead
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 2 * KB; ++kk) {
         const i32x4 pv = {(int)pw[4 * kk], (int)pw[4 * kk + 1], (int)pw[4 * kk + 2], (int)pw[4 * kk + 3]};
         const bf16x8 pop = __builtin_bit_cast(bf16x8, pv);
-        if (kk + 1 < 4) vread(kk + 1, vf[(kk + 1) & 1]);
+        if (kk + 1 < 2 * KB) vread(kk + 1, vf[(kk + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = 0; d < 4; ++d) o[d] = mfma_bf16(vf[kk & 1][d], pop, o[d]);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    if (wave_rows && (!causal || c0 + j0 <= wq_last)) {
+      if (half_tile)
+        tile_body(std::true_type{});
+      else
+        tile_body(std::false_type{});
     }
   }
 
