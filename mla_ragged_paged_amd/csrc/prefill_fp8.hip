@@ -289,6 +289,16 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = f32x16{};
+  // Row sums of the e4m3 weights of fully visible tiles, taken on the matrix core:
+  // (all-ones 32 x 64) . P^T puts each query column's sum over the tile's 64 keys
+  // in every row of the column, so lane (li, hf) reads its query's sum in
+  // lsum[0] (only that element is rescaled and read; both halves hold the whole
+  // sum).  Under the causal mask the register budget has room for the extra
+  // accumulator and operand; the null-mask kernels sum on the VALU.
+  constexpr bool MFMA_ROWSUM = CAUSAL;
+  f32x16 lsum = f32x16{};
+  const int one4 = 0x38383838;                       // four e4m3 1.0
+  const i32x8 ones8 = {one4, one4, one4, one4, one4, one4, one4, one4};
 
   // ---- prologue, ordered for the first tile's critical path: page ids first,
   // then the K_nope / V rows, then Q, so the K_rope loads wait for the page ids only
@@ -398,6 +408,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       m_run = m_new;
       mc = m_run * c;
       l_run *= alpha;
+      if constexpr (MFMA_ROWSUM) lsum[0] *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d) o[d] *= alpha;
     }
@@ -419,14 +430,18 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r + 2], e[kb][r + 3], wd, true);
         pq[x] = wd;
       }
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, false), ones, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, true), ones, ps1, false);
-      }
-      l_run += ps0 + ps1;
       const i32x8 pop = {pq[0], pq[1], pq[2], pq[3], pq[4], pq[5], pq[6], pq[7]};
+      if constexpr (MFMA_ROWSUM) {
+        lsum = mfma_fp8(ones8, pop, lsum);
+      } else {
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, false), ones, ps0, false);
+          ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, true), ones, ps1, false);
+        }
+        l_run += ps0 + ps1;
+      }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         int va[8];
@@ -475,7 +490,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
 
   // ---- epilogue: row sums of both halves, normalise (applying s_v), store the
   // row with its log-sum-exp (merged with an earlier partial when one is given)
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = l_run + swap_halves(l_run) + (MFMA_ROWSUM ? lsum[0] : 0.f);
   if (my_i < (int32_t)n) {
     const float inv = l_tot > 0.f ? s_v / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
