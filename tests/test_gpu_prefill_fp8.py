@@ -58,6 +58,55 @@ def test_fp8_scale_sign_and_zero(scale):
     assert report(step.out.float().cpu().numpy(), ref, BAR_FP8, f"fp8scale{scale}") <= BAR_FP8
 
 
+def _log2_scores(w, b, h):
+    """Scores of sequence b, head h in log2 units (scale * q.k * log2 e) on the exactly
+    dequantised inputs, [n_b, p_b + n_b] (keys of the sequence in cache order)."""
+    import oracle
+    t0, n = int(w.input_row_offsets[b]), int(w.n[b])
+    g0 = int((w.n[:b] + w.p[:b]).sum())
+    ctx = int(w.p[b]) + n
+    codes = lambda x: x.view(torch.uint8).cpu().numpy()
+    q = oracle.dequantize_e4m3fn(codes(w.q[t0:t0 + n, h]), w.scales["q"])
+    kn = oracle.dequantize_e4m3fn(codes(w.k_nope[g0:g0 + ctx, h]), w.scales["k_nope"])
+    kr_codes = oracle.rope_rows(w.cache.view(torch.uint8), w.spec.layer_idx, w.page_table, w.spec.page_size,
+                                w.spec.rope_col, b, range(ctx))
+    kr = oracle.dequantize_e4m3fn(kr_codes, w.scales["k_rope"])
+    return w.softmax_scale * (q @ np.concatenate([kn, kr], axis=1).T) * np.log2(np.e)
+
+
+@pytest.mark.parametrize("scale", [2.0, -2.0])
+def test_fp8_running_max_moves_on_fully_visible_tiles(scale):
+    """A large softmax scale makes a row's running maximum jump by more than the
+    kernel's lazy-rescale threshold (8 in log2 units) on key tiles that every query
+    of the row's wave fully sees, after earlier such tiles have been summed -- the
+    tiles whose weights are e4m3 and whose row sums the matrix core accumulates.
+    The case first shows on the oracle's scores that such jumps occur, then
+    compares every output."""
+    spec = workloads.Spec("rescale8", 2, (0, 0), (0, 0), 2, 128, True, "fp8", row_width=576, rope_col=512,
+                          seed=196)
+    w = workloads.build(spec, n=[160, 40], p=[700, 90])
+    w.softmax_scale = scale
+    x = _log2_scores(w, 0, 0)
+    p0 = int(w.p[0])
+    jumps = 0
+    for i in range(x.shape[0]):
+        wave_first = p0 + 32 * (i // 32)              # first query position of the row's wave
+        m = None
+        for kt in range((p0 + i) // 64 + 1):
+            keys = x[i, kt * 64:min((kt + 1) * 64, p0 + i + 1)]
+            mx = keys.max()
+            full = kt * 64 + 63 <= wave_first
+            if m is not None and mx > m + 8.0 and full:
+                jumps += 1
+            m = mx if m is None else max(m, mx)
+    say(f"fp8 scale {scale}: {jumps} running-max jumps beyond the threshold on fully visible tiles")
+    assert jumps > 0
+    step = _run(w)
+    bro, co, _ = check_plan(step, w)
+    ref = oracle_full(w, bro[0], co[0])
+    assert report(step.out.float().cpu().numpy(), ref, BAR_FP8, f"fp8rescale{scale}") <= BAR_FP8
+
+
 def test_fp8_workload_sampled():
     w = get_workload("fp8")
     say(f"fp8: B={w.batch} T={w.total_q} C={w.total_ctx} H={w.heads} scales={w.scales}")
