@@ -160,8 +160,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   // contiguous bf16 K_rope (QM 2 only): key j of the sequence is row g0 + j
   const bool contig = QM == 2 && a.rope_rows != nullptr;
   const uint32_t kv_bytes = jend > 0 ? (uint32_t)(jend - 1) * kv_row + DNOPE : 0u;
-  const auto kn_rs = rsrc(static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE, kv_bytes);
-  const auto v_rs = rsrc(static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE, kv_bytes);
+  const uint8_t* kn_base = static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE;
+  const uint8_t* v_base = static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE;
   const auto cr_rs = contig ? rsrc(static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * 128,
                                     jend > 0 ? (uint32_t)jend * 128u : 0u)
                            : rsrc(a.cache, a.cache_bytes);
@@ -224,14 +224,20 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   // K_nope and V rows of tile kt, then its K_rope rows (which need the page id).
   // Rows past the keys are filled with zeros by the range-checked loads, so no
   // stage ever holds stale or uninitialised V rows.
+  // The tile's descriptors start at its first row (scalar arithmetic; the byte
+  // count shrinks with it, so the range check still ends at the last key), and
+  // the LDS destinations come from the wave-uniform index.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto issue_kv = [&](int32_t kt, uint8_t* stage) {
-    const uint32_t jrow = (uint32_t)(kt * BN) * kv_row;
+    const uint32_t jrow = (uint32_t)(kt * BN) * kv_row;   // < kv_bytes for every tile of the unit
+    const auto kn_t = rsrc(kn_base + jrow, kv_bytes - jrow);
+    const auto v_t = rsrc(v_base + jrow, kv_bytes - jrow);
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)stage;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int m = 2 * w + u;
-      bload_lds(kn_rs, jrow + kn_off[u], st + KN_OFF + m * 1024);
-      bload_lds(v_rs, jrow + v_off[u], st + V_OFF + m * 1024);
+      const int m = 2 * wu + u;
+      bload_lds(kn_t, kn_off[u], st + KN_OFF + m * 1024);
+      bload_lds(v_t, v_off[u], st + V_OFF + m * 1024);
     }
   };
   auto issue_rope = [&](int32_t kt, uint8_t* stage, const uint32_t (&pg)[2]) {
@@ -244,7 +250,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       const uint32_t el = QM == 2 ? 2u : 1u;
       const uint32_t off = contig ? (uint32_t)j * 128u + 16u * kr_chunk[u]
                                   : (pg[u] * a.page_size + slot) * cache_row + a.rope_col * el + 16u * kr_chunk[u];
-      bload_lds(cr_rs, off, st + KR_OFF + (KRL * w + u) * 1024);
+      bload_lds(cr_rs, off, st + KR_OFF + (KRL * wu + u) * 1024);
     }
   };
 
