@@ -163,6 +163,24 @@ def _median_ms(torch, fn, reps, stream):
     return ms[len(ms) // 2], ms[0]
 
 
+def _alternating_median_ms(torch, fns, reps, stream):
+    """Median launch time of each of `fns`, timed in alternation (fn0, fn1, fn0, ...) so
+    that all of them see the same clock state of the chip."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(reps)]
+    for row in ev:
+        for fn, (e0, e1) in zip(fns, row):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    out = []
+    for i in range(len(fns)):
+        ms = sorted(row[i][0].elapsed_time(row[i][1]) for row in ev)
+        out.append(ms[len(ms) // 2])
+    return out
+
+
 def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
     """The paths beside the headline step, on the same workload:
     the null mask (every key visible), the context cut into three buffer rows
@@ -278,13 +296,13 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
     out["tp16_share"] = row
 
     # the whole step captured as a HIP graph and replayed, against eager launches
+    # (timed in alternation: back-to-back launches run at a clock that drifts)
     from mla_ragged_paged_amd.pipeline import CapturedStep
     out["graph_step"] = {}
     for wl in (w, workloads.build(workloads.SPECS["tiny"])):
         gs = PrefillStep(wl, "cuda:0")
         cs = CapturedStep(gs)
-        med_e, _ = _median_ms(torch, gs.run, reps, stream)
-        med_g, _ = _median_ms(torch, cs.replay, reps, stream)
+        med_e, med_g = _alternating_median_ms(torch, [gs.run, cs.replay], reps, stream)
         out["graph_step"][wl.spec.name] = {"eager_median_ms": round(med_e, 4), "graph_median_ms": round(med_g, 4)}
         del cs, gs
 
