@@ -24,6 +24,7 @@ SMALL_FP8 = [
     dict(n=[513], p=[0], heads=2, ps=128, width=576, rope=512),
     dict(n=[130, 40, 0, 200], p=[10, 0, 5, 64], heads=16, ps=16, width=576, rope=512),
     dict(n=[300], p=[20], heads=8, ps=64, width=576, rope=512),
+    dict(n=[90, 200, 17], p=[0, 64, 300], heads=40, ps=64, width=576, rope=512),  # 5 heads per XCD
 ]
 
 
