@@ -153,7 +153,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
                           QSPLIT ? (n - 1) * qr_row + (DQK - DNOPE) * 2 : 0u);
   // contiguous K_rope (split Q only): key j of the sequence is row g0 + j, 128 bytes
   const bool contig = QSPLIT && a.rope_rows != nullptr;
-  const uint32_t kv_bytes = jend > 0 ? (uint32_t)(jend - 1) * kv_row + DNOPE * 2 : 0u;
+  // bytes of the unit's K_nope / V rows from its first key (64-bit: one sequence's
+  // keys in a buffer row may span more than 4 GiB at 128 heads)
+  const uint64_t kv_bytes = jend > 0 ? (uint64_t)(jend - 1) * kv_row + DNOPE * 2 : 0u;
   const auto cr_rs = contig ? rsrc(static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * 128,
                                     jend > 0 ? (uint32_t)jend * 128u : 0u)
                            : rsrc(a.cache, a.cache_bytes);
@@ -207,15 +209,18 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   // Rows past the keys are filled with zeros by the range-checked loads, so no
   // stage ever holds stale or uninitialised V rows.
   // The tile's descriptors start at its first row (scalar arithmetic; the byte
-  // count shrinks with it, so the range check still ends at the last key), and
-  // the LDS destinations come from the wave-uniform index.
+  // count shrinks with it, so the range check still ends at the last key -- and
+  // is capped at 4 GiB - 1 while more remains, far beyond the few MiB a tile
+  // reads past its first row), and the LDS destinations come from the
+  // wave-uniform index.
   const uint8_t* kn_base = static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE * 2;
   const uint8_t* v_base = static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE * 2;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto issue_kv = [&](int32_t kt, int stage) {
-    const uint32_t jrow = (uint32_t)(kt * BN) * kv_row;   // < kv_bytes for every tile of the unit
-    const auto kn_t = rsrc(kn_base + jrow, kv_bytes - jrow);
-    const auto v_t = rsrc(v_base + jrow, kv_bytes - jrow);
+    const uint64_t jrow = (uint64_t)(kt * BN) * kv_row;   // < kv_bytes for every tile of the unit
+    const uint32_t left = (uint32_t)min(kv_bytes - jrow, (uint64_t)0xFFFFFFFFu);
+    const auto kn_t = rsrc(kn_base + jrow, left);
+    const auto v_t = rsrc(v_base + jrow, left);
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * STAGE;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
