@@ -13,6 +13,10 @@ roofline = the attention kernel (the dominant one): algorithmic FLOPs per launch
            against the MI355X dense MFMA peak of the compute dtype.
 cpu_baseline = the float64 oracle timed on the host on a bounded sample of the
            same workload (a subset of heads), scaled to TFLOP/s.
+configs  = each H=128 workload (dsv3, prefix, long, fp8): its attention launch
+           timed alone (mean / median / min), TFLOP/s, fraction of its own
+           dtype's MFMA peak, HBM traffic over algorithmic bytes, and its own
+           bounded oracle sample.
 Also reported: plan / gather / attention times (mean, median, min over the timed
 steps), the attention time with L2 and MALL flushed by a 512 MiB write before
 each launch (cold_cache), and the gather kernel's bandwidth on a >= 1 GiB
@@ -98,6 +102,52 @@ def cpu_baseline(w, budget_s: float):
             "sample": f"float64 numpy oracle, heads 0..{heads - 1} of {w.heads} (all {w.batch} sequences), "
                       f"{dt:.1f} s wall on the host, {threads} BLAS threads; elementwise softmax single-threaded",
             "cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas": blas}
+
+
+def config_bench(torch, name, reps=20, warmup=5, cpu_seconds=6.0):
+    """One H=128 workload's attention launch, timed alone on its launch stream after
+    `warmup` launches: mean / median / min over `reps` HIP-event intervals, TFLOP/s
+    and the fraction of its own dtype's dense MFMA peak, the HBM traffic of its
+    committed counter summary (when taken on the current kernel sources) over the
+    algorithmic bytes, and the oracle timed on a bounded sample of it (None when
+    cpu_seconds is 0)."""
+    from mla_ragged_paged_amd import workloads
+    from mla_ragged_paged_amd.pipeline import PrefillStep
+    w = workloads.build(workloads.SPECS[name])
+    flops = workloads.causal_flops(w.n, w.p, w.heads)
+    step = PrefillStep(w, "cuda:0")
+    stream = torch.cuda.current_stream()
+    step.run()
+    for _ in range(warmup):
+        step.attention(0)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step.attention(0)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    mean = sum(ms) / len(ms)
+    med = ms[len(ms) // 2]
+    peak = PEAK_TFLOPS[w.spec.dtype]
+    alg = workloads.algorithmic_bytes(w)
+    traffic = traffic_from_profiles(name, kernel_source_hash(w.spec.dtype))
+    out = {"workload": f"{name}: {w.spec.description}", "dtype": w.spec.dtype, "batch": w.batch,
+           "new_tokens": w.total_q, "context_tokens": w.total_ctx, "causal_tflop": round(flops / 1e12, 5),
+           "attention_mean_ms": round(mean, 4), "attention_median_ms": round(med, 4),
+           "attention_min_ms": round(ms[0], 4), "TFLOPs_mean": round(flops / (mean * 1e-3) / 1e12, 2),
+           "TFLOPs_median": round(flops / (med * 1e-3) / 1e12, 2), "peak_TFLOPs": peak,
+           "frac_mean": round(flops / (mean * 1e-3) / 1e12 / peak, 4),
+           "frac_median": round(flops / (med * 1e-3) / 1e12 / peak, 4),
+           "algorithmic_bytes": alg, "traffic_bytes": traffic,
+           "traffic_over_algorithmic": None if traffic is None else round(traffic / alg, 3),
+           "reps": reps, "warmup": warmup}
+    del step
+    if cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+    del w
+    torch.cuda.empty_cache()
+    return out
 
 
 def gather_bench(torch, batch=64, n_range=(8192, 24576), width=576, page_size=128, seed=11, reps=5):
@@ -331,6 +381,9 @@ def main():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload attention timings")
+    ap.add_argument("--config-cpu-seconds", type=float, default=6.0,
+                    help="oracle time budget per workload in the per-workload section")
     ap.add_argument("--no-extras", action="store_true", help="skip the cold-cache, gather-bandwidth, null-mask, buffer-row and merge measurements")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (scales HBM byte counters)")
@@ -459,6 +512,17 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         guarded("cpu_baseline", lambda: cpu_baseline(w, args.cpu_seconds))
+    if not args.no_configs:
+        # every H=128 workload: its attention alone, with a bounded oracle sample each
+        result["configs"] = {}
+        for name in ("dsv3", "prefix", "long", "fp8"):
+            print(f"[bench] config {name}", file=sys.stderr, flush=True)
+            try:
+                result["configs"][name] = config_bench(
+                    torch, name, cpu_seconds=0.0 if args.no_cpu_baseline else args.config_cpu_seconds)
+            except Exception as e:  # noqa: BLE001 -- report, keep the line
+                result["configs"][name] = {"error": f"{type(e).__name__}: {e}"}
+                print(f"[bench] config {name} failed: {e!r}", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
 
 

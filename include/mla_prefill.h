@@ -332,9 +332,9 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
  *   k_nope, v     device [rows][num_heads][128], qkv_dtype; fp8: code * (*k_scales)
  *                 and code * (*v_scale) (one fp32 per tensor).
  *   k_rope_rows   contiguous K_rope, device bf16 [rows][1][64] laid out like k_nope:
- *                 key j of sequence b uses row cache_row_offsets[b] + j (a
- *                 sequence's keys in one call must stay below 2^25 = 33,554,432:
- *                 its rows are addressed with 32-bit byte offsets).  NULL:
+ *                 key j of sequence b uses row cache_row_offsets[b] + j (each
+ *                 64-key tile is addressed from its own first row, so a
+ *                 sequence's rows may span more than 4 GiB).  NULL:
  *                 K_rope comes from the paged cache `kv` as in mla_prefill_ragged
  *                 (a bf16 cache, or an e4m3 cache with kv->scale when qkv_dtype is
  *                 MLA_FP8_E4M3FN; e4m3 K_rope is converted exactly to bf16 for its
@@ -538,7 +538,10 @@ int mla_prefill_set_debug(int on);
 const char* mla_status_string(mla_status_t status);
 
 /* The HIP error code (hipError_t as int) behind the last MLA_ERR_HIP returned on
- * the calling thread, 0 if none. */
+ * the calling thread, 0 if none.  For tests of that path: when the environment
+ * variable MLA_PREFILL_FAIL_LAUNCH holds a nonzero HIP error code as the library
+ * loads, every call that passes its host-side checks returns MLA_ERR_HIP with
+ * that code instead of enqueueing anything (no GPU is touched). */
 int mla_prefill_last_hip_error(void);
 
 #ifdef __cplusplus

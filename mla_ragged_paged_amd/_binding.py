@@ -218,6 +218,26 @@ def _shapes(T, H, rows=(), lses=()):
             raise ValueError(f"{name} must have shape {(T, H)}, got {tuple(t.shape)}")
 
 
+def _kv(H, dtype, k_nope, v):
+    """K_nope and V must be [rows, H, 128] with H and the element type of the query:
+    the kernels stride their rows by the query's head count and read them in its type."""
+    for name, t in (("k_nope", k_nope), ("v", v)):
+        if t.dim() != 3 or tuple(t.shape[1:]) != (H, 128):
+            raise ValueError(f"{name} must have shape [rows, {H}, 128], got {tuple(t.shape)}")
+        if _dtype_code(t) != _dtype_code_of(dtype):
+            raise TypeError(f"{name} must have the query's element type {dtype}, got {t.dtype}")
+    if k_nope.shape[0] != v.shape[0]:
+        raise ValueError(f"k_nope and v must have the same rows, got {k_nope.shape[0]} and {v.shape[0]}")
+
+
+def _dtype_code_of(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return MLA_BF16
+    if dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MLA_FP8_E4M3FN
+    raise TypeError(f"unsupported query dtype {dtype}")
+
+
 def _f32(t, name):
     if t is not None and t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32")
@@ -233,6 +253,7 @@ def mla_prefill_ragged(output, q, k_nope, v, k_rope: PagedCache, layer_idx, vali
     T, H, qd = q.shape
     _contiguous(output=output, q=q, k_nope=k_nope, v=v)
     _shapes(T, H, rows=[("output", output)])
+    _kv(H, q.dtype, k_nope, v)
     s = k_rope.as_struct()
     _check(_lib.mla_prefill_ragged(_ptr(output), _dtype_code(output), _ptr(q), _dtype_code(q), _ptr(k_nope),
                                    _ptr(v), ctypes.byref(s), layer_idx, _idx(valid_length, "valid_length"),
@@ -252,6 +273,7 @@ def mla_prefill_ragged_lse(output, lse, q, k_nope, v, k_rope: PagedCache, layer_
     T, H, qd = q.shape
     _contiguous(output=output, lse=lse, q=q, k_nope=k_nope, v=v, prev_output=prev_output, prev_lse=prev_lse)
     _shapes(T, H, rows=[("output", output), ("prev_output", prev_output)], lses=[("lse", lse), ("prev_lse", prev_lse)])
+    _kv(H, q.dtype, k_nope, v)
     s = k_rope.as_struct()
     _check(_lib.mla_prefill_ragged_lse(_ptr(output), _dtype_code(output), _f32(lse, "lse"),
                                        _f32(prev_output, "prev_output"), _f32(prev_lse, "prev_lse"), _ptr(q),
@@ -300,6 +322,7 @@ def mla_prefill_ragged_kvsplit(output, q, k_nope, v, k_rope: PagedCache, layer_i
     T, H, qd = q.shape
     _contiguous(output=output, lse=lse, q=q, k_nope=k_nope, v=v, workspace=workspace)
     _shapes(T, H, rows=[("output", output)], lses=[("lse", lse)])
+    _kv(H, q.dtype, k_nope, v)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = k_rope.as_struct()
     _check(_lib.mla_prefill_ragged_kvsplit(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _ptr(q),
@@ -321,6 +344,7 @@ def mla_prefill_ragged_row(output, acc, acc_lse, q, k_nope, v, k_rope: PagedCach
     T, H, qd = q.shape
     _contiguous(output=output, lse=lse, acc=acc, acc_lse=acc_lse, q=q, k_nope=k_nope, v=v)
     _shapes(T, H, rows=[("output", output), ("acc", acc)], lses=[("lse", lse), ("acc_lse", acc_lse)])
+    _kv(H, q.dtype, k_nope, v)
     s = k_rope.as_struct()
     _check(_lib.mla_prefill_ragged_row(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _f32(acc, "acc"),
                                        _f32(acc_lse, "acc_lse"), _ptr(q), _dtype_code(q), _ptr(k_nope), _ptr(v),
@@ -340,6 +364,7 @@ def mla_prefill_ragged_split(output, q_nope, q_rope, k_nope, v, kv: PagedCache, 
     T, H, qd = q_nope.shape
     _contiguous(output=output, lse=lse, q_nope=q_nope, q_rope=q_rope, k_nope=k_nope, v=v, k_rope_rows=k_rope_rows)
     _shapes(T, H, rows=[("output", output)], lses=[("lse", lse)])
+    _kv(H, q_nope.dtype, k_nope, v)
     if tuple(q_rope.shape) != (T, H, 64) or q_rope.dtype != torch.bfloat16:
         raise ValueError(f"q_rope must be bf16 of shape {(T, H, 64)}")
     if k_rope_rows is not None and (k_rope_rows.dtype != torch.bfloat16 or k_rope_rows.shape[-1] != 64):

@@ -30,6 +30,16 @@ std::mutex g_debug_mu;                 // one check at a time: the flag of a GPU
 constexpr int MAX_DEVICES = 64;
 int32_t* g_debug_flag[MAX_DEVICES] = {};
 
+// Launch-failure injection for tests of the error path: when the environment
+// variable MLA_PREFILL_FAIL_LAUNCH holds a nonzero HIP error code as the library
+// loads, every call that passes its host-side checks returns MLA_ERR_HIP with
+// that code instead of enqueueing anything.
+int fail_launch_from_env() {
+  const char* e = std::getenv("MLA_PREFILL_FAIL_LAUNCH");
+  return e ? std::atoi(e) : 0;
+}
+const int g_fail_launch = fail_launch_from_env();
+
 mla_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return MLA_OK;
   g_last_hip_error = (int)e;
@@ -54,6 +64,7 @@ mla_status_t check_cache(const mla_paged_cache_t* kv, uint32_t layer_idx) {
 // check kernel on the call's stream, then a wait for its flag.  No launch and
 // no wait when debug mode is off.
 mla_status_t debug_check(mla::CheckArgs c, void* stream) {
+  if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
   if (g_debug.load(std::memory_order_relaxed) == 0 || c.batch == 0) return MLA_OK;
   std::lock_guard<std::mutex> lock(g_debug_mu);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -146,6 +157,7 @@ mla_status_t mla_prefill_check(const mla_paged_cache_t* kv, const uint32_t* vali
   c.row_positions = row_positions;
   c.row_capacity = row_capacity;
   c.violations = violations;
+  if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
   return hip_status(mla::launch_check(c, static_cast<hipStream_t>(stream)));
 }
 
@@ -175,6 +187,7 @@ mla_status_t mla_prefill_plan(const uint32_t* input_row_offsets, uint32_t batch_
   a.cache_offsets = cache_offsets;
   a.buffer_lengths = buffer_lengths;
   a.status = device_status;
+  if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
   return hip_status(mla::launch_plan(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -216,6 +229,7 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
   while (unit > 1 && ((a.row_bytes % unit) || (a.col_bytes % unit) || (a.copy_bytes % unit) ||
                       (reinterpret_cast<uintptr_t>(a.cache) % unit) || (reinterpret_cast<uintptr_t>(out) % unit)))
     unit >>= 1;
+  if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
   return hip_status(mla::launch_gather(a, unit, static_cast<hipStream_t>(stream)));
 }
 
@@ -372,6 +386,7 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
     a.scale_log2 = c > 1e-30f ? c : 1e-30f;  // scale 0: every visible key weighs the same
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
   if (fp8) return hip_status(mla::launch_prefill_fp8(a, q_max, s));
   return hip_status(mla::launch_prefill_bf16(a, q_max, s));
 }
@@ -504,6 +519,7 @@ mla_status_t mla_prefill_latent_up(const mla_paged_cache_t* kv, uint32_t layer_i
   a.batch = batch_size;
   a.heads = num_heads;
   a.cap = buffer_token_size;
+  if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
   return hip_status(mla::launch_latent_up(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -528,6 +544,7 @@ mla_status_t mla_prefill_merge(void* output, mla_dtype_t output_dtype, float* ls
   a.lse_b = lse_b;
   a.rows = rows;
   a.out_fp32 = output_dtype == MLA_FP32 ? 1u : 0u;
+  if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
   return hip_status(mla::launch_merge(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -124,8 +124,10 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(GatherArgs a) {
         ++lo;
         next_start = __builtin_amdgcn_readfirstlane(bro[lo + 1]);
       }
-      const uint32_t pos = CO[lo] + (slot - __builtin_amdgcn_readfirstlane(bro[lo]));
-      const uint32_t page = PT[(size_t)lo * a.max_pages + pos / a.page_size];
+      // a slot past the row's last one has no position: its page is not looked up
+      // (its position could lie past the last sequence's page-table row)
+      const uint32_t pos = ok[r] ? CO[lo] + (slot - __builtin_amdgcn_readfirstlane(bro[lo])) : 0u;
+      const uint32_t page = ok[r] ? PT[(size_t)lo * a.max_pages + pos / a.page_size] : 0u;
       const size_t row = (size_t)page * a.page_size + pos % a.page_size;
       src[r] = a.cache + row * a.row_bytes + a.col_bytes;
       dst[r] = a.out + (size_t)slot * a.copy_bytes;

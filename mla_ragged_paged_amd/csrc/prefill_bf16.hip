@@ -156,9 +156,11 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   // bytes of the unit's K_nope / V rows from its first key (64-bit: one sequence's
   // keys in a buffer row may span more than 4 GiB at 128 heads)
   const uint64_t kv_bytes = jend > 0 ? (uint64_t)(jend - 1) * kv_row + DNOPE * 2 : 0u;
-  const auto cr_rs = contig ? rsrc(static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * 128,
-                                    jend > 0 ? (uint32_t)jend * 128u : 0u)
-                           : rsrc(a.cache, a.cache_bytes);
+  // paged K_rope: one descriptor over the cache layer; contiguous rows: one per
+  // tile, starting at the tile's first row (built in issue_rope, so the 32-bit
+  // byte count never has to cover more than what remains of the sequence's rows)
+  const auto cr_rs = rsrc(a.cache, a.cache_bytes);
+  const uint8_t* rr_base = contig ? static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * 128 : nullptr;
   const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
   const uint32_t cache_row = a.row_width * 2;
 
@@ -231,15 +233,18 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   };
   auto issue_rope = [&](int32_t kt, int stage, const uint32_t (&pg)[2]) {
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * STAGE;
+    const auto kr_t = contig ? rsrc(rr_base + (size_t)(kt * BN) * 128,
+                                    (uint32_t)min((uint64_t)(jend - kt * BN) * 128u, (uint64_t)0xFFFFFFFFu))
+                             : cr_rs;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int m = 2 * wu + u;
       const int32_t j = min(kt * BN + kr_row[u], jend - 1);
       const uint32_t pos = (uint32_t)(c0 + j);
       const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
-      const uint32_t off = contig ? (uint32_t)j * 128u + 16u * kr_chunk[u]
+      const uint32_t off = contig ? (uint32_t)(j - kt * BN) * 128u + 16u * kr_chunk[u]
                                   : (pg[u] * a.page_size + slot) * cache_row + a.rope_col * 2 + 16u * kr_chunk[u];
-      bload_lds(cr_rs, off, st + KR_OFF + m * 1024);
+      bload_lds(kr_t, off, st + KR_OFF + m * 1024);
     }
   };
 

@@ -236,3 +236,68 @@ def test_first_build_needs_no_library():
     build_src = text[text.index("def build()"):text.index("def smoke()")]
     assert "spec_from_file_location" in build_src
     assert "from mla_ragged_paged_amd import build" not in build_src
+
+
+def test_launch_failure_reports_hip_error_without_gpu():
+    """MLA_ERR_HIP and mla_prefill_last_hip_error(): with MLA_PREFILL_FAIL_LAUNCH set
+    as the library loads, calls that pass their host-side checks return MLA_ERR_HIP
+    carrying that HIP error code, and enqueue nothing (no GPU is touched)."""
+    import subprocess
+    import sys
+    code = r'''
+import ctypes, sys
+sys.path.insert(0, %r)
+import mla_ragged_paged_amd._binding as b
+lib = b._lib
+d = ctypes.c_void_p(256)
+s = b._Cache(data=256, dtype=0, num_layers=1, num_pages=4, page_size=16, row_width=64, rope_col=0,
+             page_table=256, max_pages_per_seq=4, cache_lengths=256, scale=None)
+r = ctypes.byref(s)
+out = []
+out.append(lib.mla_prefill_last_hip_error())
+out.append(lib.mla_prefill_plan(d, 1, r, 0, 64, 1, d, d, d, None, None))
+out.append(lib.mla_prefill_last_hip_error())
+out.append(lib.mla_prefill_gather(r, 0, 1, d, d, 0, 64, 64, d, None))
+out.append(lib.mla_prefill_ragged(d, 0, d, 0, d, d, r, 0, d, d, None, 1, 4, 2, 192, 128, 0,
+                                  ctypes.c_float(0.07), None, None, None, 0, None))
+out.append(lib.mla_prefill_merge(d, 0, None, d, d, d, d, 4, 2, 128, None))
+out.append(lib.mla_prefill_plan(None, 1, r, 0, 64, 1, d, d, d, None, None))   # host check still first
+print(" ".join(map(str, out)))
+''' % ROOT
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                         env={**os.environ, "MLA_PREFILL_FAIL_LAUNCH": "98", "MLA_PREFILL_DEBUG": "0"})
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.split() == ["0", "6", "98", "6", "6", "6", "1"], res.stdout
+
+
+def test_binding_rejects_mismatched_k_nope_and_v():
+    """K_nope / V with other heads than q, other widths, or another element type
+    than q are rejected in the binding before the library is called."""
+    import torch
+    import mla_ragged_paged_amd as m
+    T, H = 4, 2
+    q = torch.zeros((T, H, 192), dtype=torch.bfloat16)
+    out = torch.zeros((T, H, 128), dtype=torch.bfloat16)
+    ok = torch.zeros((8, H, 128), dtype=torch.bfloat16)
+    bad = {"fewer heads": torch.zeros((8, 1, 128), dtype=torch.bfloat16),
+           "other width": torch.zeros((8, H, 64), dtype=torch.bfloat16),
+           "other dtype": torch.zeros((8, H, 128), dtype=torch.float8_e4m3fn),
+           "other rows": torch.zeros((9, H, 128), dtype=torch.bfloat16)}
+    kv = m.PagedCache(torch.zeros((1, 1, 16, 1, 64), dtype=torch.bfloat16), torch.zeros((1, 1), dtype=torch.int32),
+                      torch.zeros((1,), dtype=torch.int32), 0)
+    idx = torch.zeros((2,), dtype=torch.int32)
+    for label, t in bad.items():
+        for kn, v in ((t, ok), (ok, t)):
+            if label == "other rows" and kn is ok:
+                continue
+            with pytest.raises((ValueError, TypeError)):
+                m.mla_prefill_ragged(out, q, kn, v, kv, 0, idx, idx, None, 0.1)
+            with pytest.raises((ValueError, TypeError)):
+                m.mla_prefill_ragged_lse(out.float(), None, q, kn, v, kv, 0, idx, idx, None, 0.1)
+            with pytest.raises((ValueError, TypeError)):
+                m.mla_prefill_ragged_row(out, out.float(), torch.zeros((T, H)), q, kn, v, kv, 0, idx, idx, None, 0.1)
+            with pytest.raises((ValueError, TypeError)):
+                m.mla_prefill_ragged_kvsplit(out, q, kn, v, kv, 0, idx, idx, None, 0.1, 0, None)
+            with pytest.raises((ValueError, TypeError)):
+                m.mla_prefill_ragged_split(out, q[..., :128].contiguous(), q[..., 128:].contiguous(), kn, v, kv, 0,
+                                           idx, idx, None, 0.1)
