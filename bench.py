@@ -1,8 +1,9 @@
 """Benchmark of one ragged paged MLA prefill step on one MI355X.
 
 A step is the whole hot path over one batch of synthetic, device-resident
-input: plan -> gather (the batch's cache rows into a contiguous buffer) ->
-causal MLA attention.  Prints one JSON line.
+input: plan -> gather (each cache row's K_rope window into contiguous rows laid
+out like K_nope / V) -> causal MLA attention reading those rows.  Prints one
+JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|prefix|long|fp8|tiny]
                   [--no-cpu-baseline] [--cpu-seconds S]
@@ -449,7 +450,7 @@ def main():
     khash = kernel_source_hash(dtype)
     traffic = traffic_from_profiles(spec.name, khash)
     el = 1 if dtype == "fp8" else 2
-    gather_bytes = 2.0 * w.total_ctx * w.cache.shape[4] * el
+    gather_bytes = 2.0 * w.total_ctx * step.gather_cols[1] * el      # read + write of the gathered window
     result = {
         "metric": "MLA prefill TFLOP/s (causal, H=128, bf16/fp8) and % of MFMA peak, 1 GPU",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),

@@ -21,6 +21,10 @@
  *                       contiguous rows (page "flare_mla_prefill", the q_nope /
  *                       q_rope / q_scale / k_scales overloads).
  *
+ *   mla_prefill_ragged_krope  the same attention with K_rope given as rows laid
+ *                       out like K (what mla_prefill_gather makes of the cache's
+ *                       K_rope column window).
+ *
  *   mla_prefill_latent_up  per-head K_nope / V of one buffer row, up-projected
  *                       from the latent part of the cache rows the plan row holds.
  *
@@ -277,6 +281,33 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
                                 uint32_t q_max_seq_len, void* stream);
 
 /*
+ * mla_prefill_ragged_krope -- page "flare_mla_prefill", the overload whose
+ * k_rope is a tensor rather than the paged cache; the plan of page
+ * "generic_flare_mla_prefill_ragged_paged_plan" exists so that the K/V entries
+ * of a buffer row can be gathered into contiguous rows, which mla_prefill_gather
+ * does for the K_rope column window.
+ *
+ * The attention of mla_prefill_ragged with K_rope(b, kpos) = k_rope row
+ * cache_row_offsets[b] + j (the row laid out like k_nope's key j of sequence
+ * b) instead of a cache read; start positions are cache_lengths[b].
+ *
+ *   k_rope          device [rows][1][64], qkv_dtype, 16-byte aligned; fp8 values
+ *                   stand for code * (*k_rope_scale).
+ *   k_rope_scale    device fp32 scalar: required for MLA_FP8_E4M3FN, NULL for bf16.
+ *   cache_lengths   device uint32 [batch_size], start position p_b of each sequence.
+ * All other arguments as mla_prefill_ragged.
+ * Errors: as mla_prefill_ragged.
+ */
+mla_status_t mla_prefill_ragged_krope(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
+                                      const void* k_nope, const void* v, const void* k_rope,
+                                      const float* k_rope_scale, const uint32_t* cache_lengths,
+                                      const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                      const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                      uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
+                                      float scale, const float* q_scale, const float* k_nope_scale,
+                                      const float* v_scale, uint32_t q_max_seq_len, void* stream);
+
+/*
  * mla_prefill_ragged_lse -- the attention of mla_prefill_ragged for one buffer
  * row of the plan (page "generic_flare_mla_prefill_ragged_paged_plan",
  * description and Args: a row holds part of each sequence's cached context),
@@ -331,16 +362,20 @@ mla_status_t mla_prefill_ragged_lse(void* output, mla_dtype_t output_dtype, floa
  *   q_rope        device [total_q_tokens][num_heads][64], bf16, never scaled.
  *   k_nope, v     device [rows][num_heads][128], qkv_dtype; fp8: code * (*k_scales)
  *                 and code * (*v_scale) (one fp32 per tensor).
- *   k_rope_rows   contiguous K_rope, device bf16 [rows][1][64] laid out like k_nope:
+ *   k_rope_rows   contiguous K_rope, device [rows][1][64] laid out like k_nope:
  *                 key j of sequence b uses row cache_row_offsets[b] + j (each
  *                 64-key tile is addressed from its own first row, so a
- *                 sequence's rows may span more than 4 GiB).  NULL:
+ *                 sequence's rows may span more than 4 GiB).  Their element
+ *                 type is kv->dtype: bf16, or e4m3 (qkv_dtype MLA_FP8_E4M3FN
+ *                 only) standing for code * (*kv->scale), converted exactly to
+ *                 bf16 for its product with q_rope.  NULL:
  *                 K_rope comes from the paged cache `kv` as in mla_prefill_ragged
  *                 (a bf16 cache, or an e4m3 cache with kv->scale when qkv_dtype is
  *                 MLA_FP8_E4M3FN; e4m3 K_rope is converted exactly to bf16 for its
  *                 product with q_rope).
  *   kv            [host] cache descriptor.  With k_rope_rows only kv->cache_lengths
- *                 (the start positions) is read.
+ *                 (the start positions), kv->dtype and kv->scale (the rows'
+ *                 element type and scale) are read.
  *   q_scale, k_scales, v_scale  device fp32 scalars, required for MLA_FP8_E4M3FN
  *                 and NULL for MLA_BF16.
  * Other arguments as in mla_prefill_ragged; depth must be 128.  output is bf16

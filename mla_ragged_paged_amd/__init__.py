@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     mla_prefill_latent_up,
     mla_prefill_merge,
     mla_prefill_ragged,
+    mla_prefill_ragged_krope,
     mla_prefill_ragged_kvsplit,
     mla_prefill_ragged_lse,
     mla_prefill_ragged_row,

@@ -85,6 +85,9 @@ def _load():
     lib.mla_prefill_ragged_kvsplit.restype = i32
     lib.mla_prefill_kvsplit_workspace_bytes.argtypes = [u32, u32]
     lib.mla_prefill_kvsplit_workspace_bytes.restype = ctypes.c_uint64
+    lib.mla_prefill_ragged_krope.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32, u32, u32, u32, u32,
+                                             i32, ctypes.c_float, vp, vp, vp, u32, vp]
+    lib.mla_prefill_ragged_krope.restype = i32
     lib.mla_prefill_latent_up.argtypes = [cp, u32, u32, vp, vp, u32, u32, vp, u32, u32, vp, vp, vp]
     lib.mla_prefill_latent_up.restype = i32
     lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
@@ -358,21 +361,26 @@ def mla_prefill_ragged_row(output, acc, acc_lse, q, k_nope, v, k_rope: PagedCach
 
 def mla_prefill_ragged_split(output, q_nope, q_rope, k_nope, v, kv: PagedCache, layer_idx, valid_length,
                              cache_row_offsets, cache_offsets, scale, q_scale=None, k_scales=None, v_scale=None,
-                             k_rope_rows=None, lse=None, q_max_seq_len=0, stream=None, mask="causal"):
+                             k_rope_rows=None, lse=None, q_max_seq_len=0, stream=None, mask="causal",
+                             k_rope_scale=None):
     """Split-query attention: q_nope [T, H, 128] (bf16 or fp8 with q_scale), q_rope [T, H, 64] bf16;
-    K_rope from ``kv`` (paged) or from contiguous bf16 rows ``k_rope_rows`` [rows, 1, 64]."""
+    K_rope from ``kv`` (paged) or from contiguous rows ``k_rope_rows`` [rows, 1, 64], bf16 or
+    (with an fp8 q_nope) float8_e4m3fn with its scale ``k_rope_scale`` ([1] float32)."""
     T, H, qd = q_nope.shape
     _contiguous(output=output, lse=lse, q_nope=q_nope, q_rope=q_rope, k_nope=k_nope, v=v, k_rope_rows=k_rope_rows)
     _shapes(T, H, rows=[("output", output)], lses=[("lse", lse)])
     _kv(H, q_nope.dtype, k_nope, v)
     if tuple(q_rope.shape) != (T, H, 64) or q_rope.dtype != torch.bfloat16:
         raise ValueError(f"q_rope must be bf16 of shape {(T, H, 64)}")
-    if k_rope_rows is not None and (k_rope_rows.dtype != torch.bfloat16 or k_rope_rows.shape[-1] != 64):
-        raise ValueError("k_rope_rows must be bf16 [rows, 1, 64]")
     if k_rope_rows is not None:
-        s = _Cache(data=None, dtype=_dtype_code(q_nope), num_layers=0, num_pages=0, page_size=0, row_width=0,
+        if k_rope_rows.shape[-1] != 64 or k_rope_rows.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+            raise ValueError("k_rope_rows must be bf16 or float8_e4m3fn [rows, 1, 64]")
+        if (k_rope_rows.dtype == torch.float8_e4m3fn) != (k_rope_scale is not None):
+            raise ValueError("e4m3 k_rope_rows need k_rope_scale (and bf16 rows take none)")
+        s = _Cache(data=None, dtype=_dtype_code(k_rope_rows), num_layers=0, num_pages=0, page_size=0, row_width=0,
                    rope_col=0, page_table=None, max_pages_per_seq=0,
-                   cache_lengths=_idx(kv.cache_lengths, "cache_lengths").value, scale=None)
+                   cache_lengths=_idx(kv.cache_lengths, "cache_lengths").value,
+                   scale=None if k_rope_scale is None else k_rope_scale.data_ptr())
     else:
         s = kv.as_struct()
     _check(_lib.mla_prefill_ragged_split(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _ptr(q_nope),
@@ -384,6 +392,27 @@ def mla_prefill_ragged_split(output, q_nope, q_rope, k_nope, v, kv: PagedCache, 
                                          k_nope.shape[2], _mask_code(mask), float(scale), int(q_max_seq_len),
                                          _stream(stream)),
            "mla_prefill_ragged_split")
+
+
+def mla_prefill_ragged_krope(output, q, k_nope, v, k_rope, cache_lengths, valid_length, cache_row_offsets,
+                             cache_offsets, scale, k_rope_scale=None, q_scale=None, k_nope_scale=None, v_scale=None,
+                             q_max_seq_len=0, stream=None, mask="causal"):
+    """Attention with K_rope given as rows laid out like K: k_rope [rows, 1, 64] of q's element
+    type (float8_e4m3fn with k_rope_scale [1] float32), start positions cache_lengths [B]."""
+    T, H, qd = q.shape
+    _contiguous(output=output, q=q, k_nope=k_nope, v=v, k_rope=k_rope)
+    _shapes(T, H, rows=[("output", output)])
+    _kv(H, q.dtype, k_nope, v)
+    if k_rope.dim() != 3 or tuple(k_rope.shape[1:]) != (1, 64) or _dtype_code(k_rope) != _dtype_code(q):
+        raise ValueError(f"k_rope must be [rows, 1, 64] of q's element type, got {tuple(k_rope.shape)} {k_rope.dtype}")
+    _check(_lib.mla_prefill_ragged_krope(_ptr(output), _dtype_code(output), _ptr(q), _dtype_code(q), _ptr(k_nope),
+                                         _ptr(v), _ptr(k_rope), _f32(k_rope_scale, "k_rope_scale"),
+                                         _idx(cache_lengths, "cache_lengths"), _idx(valid_length, "valid_length"),
+                                         _idx(cache_row_offsets, "cache_row_offsets"),
+                                         _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H, qd,
+                                         k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
+                                         _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
+           "mla_prefill_ragged_krope")
 
 
 def mla_prefill_latent_up(kv: PagedCache, layer_idx, buffer_row_offsets_r, cache_offsets_r, w_kv, k_nope, v,

@@ -237,13 +237,14 @@ mla_status_t mla_prefill_gather(const mla_paged_cache_t* kv, uint32_t layer_idx,
 
 namespace {
 
-// Query and K_rope sources of a call: one q [T][H][192] and K_rope from the
-// paged cache, or (split) q_nope [T][H][128] + bf16 q_rope [T][H][64] with K_rope
-// from the paged cache or from contiguous bf16 rows laid out like K.
+// Query and K_rope sources of a call: one q [T][H][192], or (split) q_nope
+// [T][H][128] + bf16 q_rope [T][H][64]; K_rope from the paged cache, or from
+// contiguous rows laid out like K (their element type and scale in the cache
+// descriptor's dtype and scale).
 struct QuerySource {
   const void* q;           // q, or q_nope when split
   const void* q_rope;      // split only
-  const void* rope_rows;   // split only, may be NULL (paged)
+  const void* rope_rows;   // NULL: K_rope from the paged cache
   bool split;
 };
 
@@ -274,10 +275,12 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
   if (qs.split && !qs.q_rope) return MLA_ERR_NULL_ARG;
   if ((prev_output == nullptr) != (prev_lse == nullptr)) return MLA_ERR_NULL_ARG;
   if (row_mode && (!acc || !acc_lse)) return MLA_ERR_NULL_ARG;
-  const bool contig = qs.split && qs.rope_rows != nullptr;
+  const bool contig = qs.rope_rows != nullptr;
   if (contig) {
-    // K_rope rows are given; the cache descriptor supplies the start positions only
+    // K_rope rows are given; the cache descriptor supplies the start positions
+    // and the rows' element type and scale
     if (!k_rope || !k_rope->cache_lengths) return MLA_ERR_NULL_ARG;
+    if (!dtype_known(k_rope->dtype)) return MLA_ERR_UNSUPPORTED_DTYPE;
   } else {
     mla_status_t st = check_cache(k_rope, layer_idx);
     if (st != MLA_OK) return st;
@@ -287,13 +290,11 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
   if (!dtype_known(qkv_dtype) || (output_dtype != MLA_BF16 && output_dtype != MLA_FP32))
     return MLA_ERR_UNSUPPORTED_DTYPE;
   const bool fp8 = qkv_dtype == MLA_FP8_E4M3FN;
-  // K_rope's type: the cache's (it must match q's for a full query; a split query
-  // takes a bf16 cache, or an e4m3 one with e4m3 q_nope), bf16 for contiguous rows
-  const bool rope_fp8 = !contig && k_rope->dtype == MLA_FP8_E4M3FN;
-  if (!contig) {
-    if (!qs.split && k_rope->dtype != qkv_dtype) return MLA_ERR_UNSUPPORTED_DTYPE;
-    if (qs.split && rope_fp8 && !fp8) return MLA_ERR_UNSUPPORTED_DTYPE;
-  }
+  // K_rope's type: the descriptor's (it must match q's for a full query; a split
+  // query takes bf16 K_rope, or e4m3 K_rope with e4m3 q_nope)
+  const bool rope_fp8 = k_rope->dtype == MLA_FP8_E4M3FN;
+  if (!qs.split && k_rope->dtype != qkv_dtype) return MLA_ERR_UNSUPPORTED_DTYPE;
+  if (qs.split && rope_fp8 && !fp8) return MLA_ERR_UNSUPPORTED_DTYPE;
   if (fp8 && (!q_scale || !k_nope_scale || !v_scale)) return MLA_ERR_NULL_ARG;
   if (rope_fp8 && !k_rope->scale) return MLA_ERR_NULL_ARG;
   if (!fp8 && (q_scale || k_nope_scale || v_scale)) return MLA_ERR_UNSUPPORTED_DTYPE;
@@ -357,10 +358,10 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
   a.k_nope = k_nope;
   a.v = v;
   a.cache_lengths = k_rope->cache_lengths;
+  a.k_rope_scale = k_rope->scale;
   if (!contig) {
     a.cache = layer_base(k_rope, layer_idx);
     a.page_table = k_rope->page_table;
-    a.k_rope_scale = k_rope->scale;
     a.max_pages = k_rope->max_pages_per_seq;
     a.page_size = k_rope->page_size;
     a.page_shift = (k_rope->page_size & (k_rope->page_size - 1)) == 0 ? (uint32_t)__builtin_ctz(k_rope->page_size)
@@ -436,6 +437,28 @@ mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const vo
                       v, k_rope, layer_idx, valid_length, cache_row_offsets, cache_offsets, batch_size,
                       total_q_tokens, num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale,
                       q_max_seq_len, stream);
+}
+
+mla_status_t mla_prefill_ragged_krope(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
+                                      const void* k_nope, const void* v, const void* k_rope,
+                                      const float* k_rope_scale, const uint32_t* cache_lengths,
+                                      const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                      const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
+                                      uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask,
+                                      float scale, const float* q_scale, const float* k_nope_scale,
+                                      const float* v_scale, uint32_t q_max_seq_len, void* stream) {
+  if (!k_rope || !cache_lengths) return MLA_ERR_NULL_ARG;
+  // the rows' element type is the query's; only the start positions and the
+  // rows' scale are taken from this descriptor
+  mla_paged_cache_t rows{};
+  rows.dtype = qkv_dtype;
+  rows.cache_lengths = cache_lengths;
+  rows.scale = k_rope_scale;
+  if (qkv_dtype != MLA_FP8_E4M3FN && k_rope_scale) return MLA_ERR_UNSUPPORTED_DTYPE;
+  return prefill_impl(output, output_dtype, nullptr, nullptr, nullptr, nullptr, nullptr, false,
+                      QuerySource{q, nullptr, k_rope, false}, qkv_dtype, k_nope, v, &rows, 0, valid_length,
+                      cache_row_offsets, cache_offsets, batch_size, total_q_tokens, num_heads, q_depth, depth, mask,
+                      scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream);
 }
 
 mla_status_t mla_prefill_ragged_kvsplit(void* output, mla_dtype_t output_dtype, float* lse, const void* q,

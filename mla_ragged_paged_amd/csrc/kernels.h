@@ -69,7 +69,8 @@ struct PrefillArgs {
   float* acc_lse;                     // row mode: [T][H]
   uint32_t row_mode;                  // 1: one plan row of several, called in row order
   const void* q_rope;                 // split Q: bf16 [T][H][64] (q then holds q_nope [T][H][128])
-  const void* rope_rows;              // contiguous bf16 K_rope [rows][64] laid out like K, or nullptr (paged)
+  const void* rope_rows;              // contiguous K_rope [rows][64] laid out like K (bf16, or e4m3 with
+                                      // k_rope_scale), or nullptr (paged)
   uint32_t q_split;                   // 1: Q comes as q_nope (a.q) + q_rope
   float* ws;                          // key split: [2][T][H][128] fp32 partial rows, then [2][T][H] lse
   uint32_t split_keys;                // key split: tiles seeing more keys are split in two; 0 = none

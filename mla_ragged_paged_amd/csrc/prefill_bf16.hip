@@ -80,8 +80,8 @@ __device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 // CAUSAL: causal mask, else the null mask.  PLAIN: bf16 output only (no
 // log-sum-exp, no earlier partial to merge).  QSPLIT: the query comes as q_nope
-// [T][H][128] and q_rope [T][H][64], and K_rope may be given as contiguous rows
-// laid out like K (else it is read through the page table).  KVSPLIT: the grid
+// [T][H][128] and q_rope [T][H][64].  K_rope is read through the page table, or
+// from contiguous rows laid out like K when a.rope_rows is set.  KVSPLIT: the grid
 // holds two units per query tile, and a tile that kv_split_tile selects is
 // computed as two halves of its key tiles into the workspace (full query only).
 template <bool CAUSAL, bool PLAIN, bool QSPLIT, bool KVSPLIT>
@@ -151,8 +151,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const auto qr_rs = rsrc(QSPLIT ? static_cast<const uint8_t*>(a.q_rope) + ((size_t)t0 * H + h) * (DQK - DNOPE) * 2
                                  : nullptr,
                           QSPLIT ? (n - 1) * qr_row + (DQK - DNOPE) * 2 : 0u);
-  // contiguous K_rope (split Q only): key j of the sequence is row g0 + j, 128 bytes
-  const bool contig = QSPLIT && a.rope_rows != nullptr;
+  // contiguous K_rope rows laid out like K: key j of the sequence is row g0 + j, 128 bytes
+  const bool contig = a.rope_rows != nullptr;
   // bytes of the unit's K_nope / V rows from its first key (64-bit: one sequence's
   // keys in a buffer row may span more than 4 GiB at 128 heads)
   const uint64_t kv_bytes = jend > 0 ? (uint64_t)(jend - 1) * kv_row + DNOPE * 2 : 0u;
@@ -218,12 +218,11 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const uint8_t* kn_base = static_cast<const uint8_t*>(a.k_nope) + ((size_t)g0 * H + h) * DNOPE * 2;
   const uint8_t* v_base = static_cast<const uint8_t*>(a.v) + ((size_t)g0 * H + h) * DNOPE * 2;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto issue_kv = [&](int32_t kt, int stage) {
+  auto issue_kv = [&](int32_t kt, MLA_LDS uint8_t* st) {
     const uint64_t jrow = (uint64_t)(kt * BN) * kv_row;   // < kv_bytes for every tile of the unit
     const uint32_t left = (uint32_t)min(kv_bytes - jrow, (uint64_t)0xFFFFFFFFu);
     const auto kn_t = rsrc(kn_base + jrow, left);
     const auto v_t = rsrc(v_base + jrow, left);
-    MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * STAGE;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int m = 4 * wu + u;
@@ -231,8 +230,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       bload_lds(v_t, v_off[u], st + V_OFF + m * 1024);
     }
   };
-  auto issue_rope = [&](int32_t kt, int stage, const uint32_t (&pg)[2]) {
-    MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * STAGE;
+  auto issue_rope = [&](int32_t kt, MLA_LDS uint8_t* st, const uint32_t (&pg)[2]) {
     const auto kr_t = contig ? rsrc(rr_base + (size_t)(kt * BN) * 128,
                                     (uint32_t)min((uint64_t)(jend - kt * BN) * 128u, (uint64_t)0xFFFFFFFFu))
                              : cr_rs;
@@ -290,11 +288,11 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     // HBM traffic where others gave up to 19x.)
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    issue_kv(kt_lo, kt_lo & 1);
+    issue_kv(kt_lo, (MLA_LDS uint8_t*)lds + (kt_lo & 1) * STAGE);
     __builtin_amdgcn_sched_barrier(0);
     load_q();
     __builtin_amdgcn_sched_barrier(0);
-    issue_rope(kt_lo, kt_lo & 1, pg0);
+    issue_rope(kt_lo, (MLA_LDS uint8_t*)lds + (kt_lo & 1) * STAGE, pg0);
   } else {
     // With no key to attend to, Q is never read (the epilogue writes 0 or passes
     // an earlier partial through).  The load stays: without this branch the
@@ -313,9 +311,15 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       for (int ks = 0; ks < 12; ++ks)
         qop[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(i32x4, qop[ks]) ^ (int)0x80008000);
     }
+    // The stage loaded here and the stage read below are the two disjoint halves
+    // of the LDS buffer.  They reach the tile code as restrict pointers of one
+    // inlined call, so the compiler can tell that reads of this tile do not depend
+    // on the next tile's direct-to-LDS loads and does not wait for those (the
+    // wait at the top of the next iteration and the barrier order them instead).
+    auto step = [&](MLA_LDS uint8_t* __restrict__ ld, const MLA_LDS uint8_t* __restrict__ rd) {
     if (kt + 1 < kt_hi) {
-      issue_kv(kt + 1, stage ^ 1);
-      issue_rope(kt + 1, stage ^ 1, pg_next);
+      issue_kv(kt + 1, ld);
+      issue_rope(kt + 1, ld, pg_next);
       pg_next[0] = page_of(kt + 2, 0);
       pg_next[1] = page_of(kt + 2, 1);
     }
@@ -327,7 +331,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     auto tile_body = [&](auto half_c) {
       constexpr bool HALF = decltype(half_c)::value;
       constexpr int KB = HALF ? 1 : 2;                 // key blocks of 32 this wave computes
-      const uint8_t* st = lds + stage * STAGE;
+      const MLA_LDS uint8_t* st = rd;
       // S^T = K Q^T.  K fragments go through a three-deep register ring, read two
       // k-steps ahead of their MFMAs so LDS latency overlaps the MFMA chain; the
       // scheduling barriers keep the compiler from sinking the reads to their uses.
@@ -337,7 +341,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const uint32_t off = ks < 8 ? kn_rd[ks] + kb * 32 * 256 : kr_rd[ks - 8] + kb * 32 * 128;
-          dst[kb] = *reinterpret_cast<const bf16x8*>(st + off);
+          dst[kb] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + off);
         }
       };
       kread(0, kf[0]);
@@ -369,7 +373,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       auto vread = [&](int kk, bf16x8 (&dst)[4]) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const MLA_LDS uint8_t* base = (const MLA_LDS uint8_t*)st + v_rd[d] + kk * 16 * 256;
+          const MLA_LDS uint8_t* base = st + v_rd[d] + kk * 16 * 256;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(base + 8 * 256));
           dst[d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -428,6 +432,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       else
         tile_body(std::false_type{});
     }
+    };
+    step((MLA_LDS uint8_t*)lds + (stage ^ 1) * STAGE, (const MLA_LDS uint8_t*)lds + stage * STAGE);
   }
 
   // ---- epilogue: combine the two halves' row sums, normalise, store the row

@@ -75,10 +75,11 @@ __device__ __forceinline__ i32x2 e4m3x4_to_bf16x4(int x) {
 
 // CAUSAL: causal mask, else the null mask.  PLAIN: bf16 output only (no
 // log-sum-exp, no earlier partial to merge).  QM: how the query and K_rope come:
-//   0  q [T][H][192] e4m3 with q_scale; K_rope e4m3 from the paged cache;
+//   0  q [T][H][192] e4m3 with q_scale; K_rope e4m3 from the paged cache or
+//      from contiguous rows laid out like K (with their scale in k_rope_scale);
 //   1  split: q_nope [T][H][128] e4m3 with q_scale and q_rope [T][H][64] bf16;
-//      K_rope e4m3 from the paged cache, converted exactly to bf16 for the rope
-//      product, which runs on the bf16 MFMA;
+//      K_rope e4m3 (paged cache or contiguous rows), converted exactly to bf16
+//      for the rope product, which runs on the bf16 MFMA;
 //   2  split as 1, K_rope bf16 (paged bf16 cache or contiguous rows laid out like K).
 // KVSPLIT: the grid holds two units per query tile, and a tile that
 // kv_split_tile selects is computed as two halves of its key tiles into the
@@ -157,8 +158,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   const auto qr_rs = rsrc(QM != 0 ? static_cast<const uint8_t*>(a.q_rope) + ((size_t)t0 * H + h) * (DQK - DNOPE) * 2
                                   : nullptr,
                           QM != 0 ? (n - 1) * qr_row + (DQK - DNOPE) * 2 : 0u);
-  // contiguous bf16 K_rope (QM 2 only): key j of the sequence is row g0 + j
-  const bool contig = QM == 2 && a.rope_rows != nullptr;
+  // contiguous K_rope rows (e4m3, or bf16 with QM 2): key j of the sequence is row g0 + j
+  const bool contig = a.rope_rows != nullptr;
   // bytes of the unit's K_nope / V rows from its first key (64-bit: one sequence's
   // keys in a buffer row may span more than 4 GiB at 128 heads)
   const uint64_t kv_bytes = jend > 0 ? (uint64_t)(jend - 1) * kv_row + DNOPE : 0u;
@@ -168,7 +169,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   // tile, starting at the tile's first row (built in issue_rope, so the 32-bit
   // byte count never has to cover more than what remains of the sequence's rows)
   const auto cr_rs = rsrc(a.cache, a.cache_bytes);
-  const uint8_t* rr_base = contig ? static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * 128 : nullptr;
+  const uint8_t* rr_base = contig ? static_cast<const uint8_t*>(a.rope_rows) + (size_t)g0 * KR_ROW : nullptr;
   const uint32_t* __restrict__ PT = a.page_table + (size_t)b * a.max_pages;
   const uint32_t cache_row = a.row_width * (QM == 2 ? 2u : 1u);   // bytes of one cache row
 
@@ -249,8 +250,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   };
   auto issue_rope = [&](int32_t kt, uint8_t* stage, const uint32_t (&pg)[2]) {
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)stage;
-    const auto kr_t = contig ? rsrc(rr_base + (size_t)(kt * BN) * 128,
-                                    (uint32_t)min((uint64_t)(jend - kt * BN) * 128u, (uint64_t)0xFFFFFFFFu))
+    const auto kr_t = contig ? rsrc(rr_base + (size_t)(kt * BN) * KR_ROW,
+                                    (uint32_t)min((uint64_t)(jend - kt * BN) * KR_ROW, (uint64_t)0xFFFFFFFFu))
                              : cr_rs;
 #pragma unroll
     for (int u = 0; u < KRL; ++u) {
@@ -258,7 +259,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       const uint32_t pos = (uint32_t)(c0 + j);
       const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
       const uint32_t el = QM == 2 ? 2u : 1u;
-      const uint32_t off = contig ? (uint32_t)(j - kt * BN) * 128u + 16u * kr_chunk[u]
+      const uint32_t off = contig ? (uint32_t)(j - kt * BN) * (uint32_t)KR_ROW + 16u * kr_chunk[u]
                                   : (pg[u] * a.page_size + slot) * cache_row + a.rope_col * el + 16u * kr_chunk[u];
       bload_lds(kr_t, off, st + KR_OFF + (KRL * wu + u) * 1024);
     }

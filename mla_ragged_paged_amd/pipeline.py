@@ -4,6 +4,11 @@ Holds a workload's tensors in device memory, allocates the plan, gather and
 output buffers once, and calls the C entry points on the current stream.  No
 arithmetic of the method happens here.
 
+By default the gather copies each buffer row's K_rope column window of the
+cache rows into contiguous rows laid out like K_nope / V, and the attention of a
+one-row plan reads K_rope from those rows (mla_prefill_ragged_krope); other
+attention calls read K_rope through the page table.
+
 With a buffer-row capacity below the batch's context the plan makes several
 rows; each row's attention is a partial softmax over the keys the row holds,
 and the rows are combined through their log-sum-exps (the merge is fused into
@@ -57,7 +62,8 @@ class PrefillStep:
 
     ``cap`` is the buffer-row capacity handed to the plan (default: the whole
     batch's context, one row).  ``gather_cols`` = (col_begin, col_count) of the
-    cache rows the gather copies (default: the whole row).  With ``kv_b_weight``
+    cache rows the gather copies (default: the 64-column K_rope window, which the
+    attention of a one-row plan then reads; any other window is gathered only).  With ``kv_b_weight``
     ([H*256, latent_dim] bf16) K_nope / V are not the workload's tensors but are
     decompressed per buffer row from the latent cache (columns
     ``latent_col`` .. +latent_dim), which replaces the gather step.
@@ -94,8 +100,8 @@ class PrefillStep:
         self.cache_offsets = torch.zeros((self.rows, Bsz), dtype=torch.int32, device=dev)
         self.buffer_lengths = torch.zeros((self.rows,), dtype=torch.int32, device=dev)
         self.status = torch.zeros((1,), dtype=torch.int32, device=dev)
-        width = w.cache.shape[4]
-        self.gather_cols = (0, width) if gather_cols is None else tuple(gather_cols)
+        self.rope_gather = gather_cols is None and kv_b_weight is None
+        self.gather_cols = (w.spec.rope_col, 64) if gather_cols is None else tuple(gather_cols)
         self.gathered = torch.zeros((self.cap, self.gather_cols[1]), dtype=w.cache.dtype, device=dev)
         self.out = torch.zeros((w.total_q, w.heads, 128), dtype=torch.bfloat16, device=dev)
         self.kv_b_weight = None if kv_b_weight is None else kv_b_weight.to(dev).contiguous()
@@ -143,10 +149,22 @@ class PrefillStep:
                                 self.kv_b_weight, self.kn_buf, self.v_buf, latent_col=self.latent_col,
                                 latent_dim=self.kv_b_weight.shape[1], stream=stream)
 
-    def attention(self, row: int = 0, k_nope=None, v=None, out=None, cache_offsets="plan", stream=None):
-        """Attention over plan row ``row``; k_nope / v default to the workload's buffer (one-row layout)."""
+    def attention(self, row: int = 0, k_nope=None, v=None, out=None, cache_offsets="plan", stream=None,
+                  rope="gathered"):
+        """Attention over plan row ``row``; k_nope / v default to the workload's buffer (one-row layout).
+        K_rope comes from the gathered rows when the step gathers them and the plan has one
+        row (``rope="gathered"``), else (or with ``rope="paged"``) through the page table."""
         co = self.cache_offsets[row] if isinstance(cache_offsets, str) else cache_offsets
         sc = self.scales or {}
+        if rope == "gathered" and self.rope_gather and self.rows == 1 and not self.split_keys:
+            B.mla_prefill_ragged_krope(self.out if out is None else out, self.q,
+                                       self.k_nope if k_nope is None else k_nope, self.v if v is None else v,
+                                       self.gathered.view(self.cap, 1, 64), self.cache_lengths,
+                                       self.input_row_offsets, self.buffer_row_offsets[row], co, self.w.softmax_scale,
+                                       k_rope_scale=sc.get("k_rope"), q_scale=sc.get("q"),
+                                       k_nope_scale=sc.get("k_nope"), v_scale=sc.get("v"), q_max_seq_len=self.w.max_q,
+                                       stream=stream, mask=self.mask)
+            return
         if self.split_keys:
             B.mla_prefill_ragged_kvsplit(self.out if out is None else out, self.q,
                                          self.k_nope if k_nope is None else k_nope, self.v if v is None else v,

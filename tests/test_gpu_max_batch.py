@@ -59,7 +59,7 @@ def w():
 def test_plan_gather_at_max_batch(w):
     say(f"max batch: B={w.batch} T={w.total_q} C={w.total_ctx}")
     for cap in (None, -(-w.total_ctx // 3)):
-        step = PrefillStep(w, "cuda", cap=cap)
+        step = PrefillStep(w, "cuda", cap=cap, gather_cols=(0, 576))   # whole cache rows
         step.plan()
         torch.cuda.synchronize()
         bro, co, _ = check_plan(step, w)

@@ -16,7 +16,7 @@ def test_plan_and_gather_on_workloads(name):
     spec = workloads.SPECS[name]
     say(f"plan+gather {name}: {spec.description}")
     w = get_workload(name)
-    step = PrefillStep(w, "cuda")
+    step = PrefillStep(w, "cuda", gather_cols=(0, w.cache.shape[4]))   # whole cache rows
     step.plan()
     step.gather(0)
     torch.cuda.synchronize()

@@ -59,7 +59,7 @@ def test_random_batches_plan_gather_attention(c):
     C = w.total_ctx
     cap = max(1, -(-C // c["cap_div"]))
     # plan and gather over every row of a plan with capacity C / cap_div
-    step = PrefillStep(w, "cuda", cap=cap)
+    step = PrefillStep(w, "cuda", cap=cap, gather_cols=(0, w.cache.shape[4]))   # whole cache rows
     step.plan()
     torch.cuda.synchronize()
     bro, co, bl = check_plan(step, w)

@@ -30,9 +30,9 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["mla_prefill_check", "mla_prefill_gather", "mla_prefill_kvsplit_workspace_bytes",
                                     "mla_prefill_last_hip_error", "mla_prefill_latent_up", "mla_prefill_merge",
-                                    "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_kvsplit",
-                                    "mla_prefill_ragged_lse", "mla_prefill_ragged_row", "mla_prefill_ragged_split",
-                                    "mla_prefill_set_debug", "mla_status_string"]
+                                    "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_krope",
+                                    "mla_prefill_ragged_kvsplit", "mla_prefill_ragged_lse", "mla_prefill_ragged_row",
+                                    "mla_prefill_ragged_split", "mla_prefill_set_debug", "mla_status_string"]
 
 
 def test_binding_exposes_every_entry_point():
@@ -301,3 +301,25 @@ def test_binding_rejects_mismatched_k_nope_and_v():
             with pytest.raises((ValueError, TypeError)):
                 m.mla_prefill_ragged_split(out, q[..., :128].contiguous(), q[..., 128:].contiguous(), kn, v, kv, 0,
                                            idx, idx, None, 0.1)
+
+
+def test_krope_validation_without_gpu():
+    """mla_prefill_ragged_krope: host-side checks return their codes before anything is enqueued."""
+    import mla_ragged_paged_amd._binding as b
+    lib = b._lib
+    d = ctypes.c_void_p(256)
+
+    def args(**kw):
+        return [kw.get("out", d), kw.get("odt", 0), d, kw.get("qdt", 0), d, d, kw.get("rows", d), kw.get("rs"),
+                kw.get("cl", d), d, d, None, kw.get("b", 1), 4, 2, kw.get("qd", 192), 128, kw.get("mask", 0),
+                ctypes.c_float(0.07), kw.get("qs"), kw.get("qs"), kw.get("qs"), 0, None]
+    assert lib.mla_prefill_ragged_krope(*args(rows=None)) == 1                # no K_rope rows
+    assert lib.mla_prefill_ragged_krope(*args(cl=None)) == 1                  # no start positions
+    assert lib.mla_prefill_ragged_krope(*args(rs=d)) == 3                     # a rows scale for bf16
+    assert lib.mla_prefill_ragged_krope(*args(qdt=1, qs=d)) == 1              # e4m3 rows without their scale
+    assert lib.mla_prefill_ragged_krope(*args(qdt=2)) == 3                    # fp32 inputs
+    assert lib.mla_prefill_ragged_krope(*args(qd=128)) == 4
+    assert lib.mla_prefill_ragged_krope(*args(mask=3)) == 5
+    assert lib.mla_prefill_ragged_krope(*args(rows=ctypes.c_void_p(264))) == 2   # rows not 16-byte aligned
+    assert lib.mla_prefill_ragged_krope(*args(out=None)) == 1
+    assert lib.mla_prefill_ragged_krope(*args(b=0)) == 0                      # empty batch: a no-op
