@@ -445,6 +445,38 @@ mla_status_t mla_prefill_ragged_kvsplit(void* output, mla_dtype_t output_dtype, 
  * token and head). */
 uint64_t mla_prefill_kvsplit_workspace_bytes(uint32_t total_q_tokens, uint32_t num_heads);
 
+/* Bytes of the scratch array of mla_prefill_ragged_kvsplit_noalloc (64 MiB):
+ * split calls with mla_prefill_kvsplit_workspace_bytes(total_q_tokens,
+ * num_heads) up to this size, i.e. total_q_tokens * num_heads <= 65,027. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * mla_prefill_ragged_kvsplit_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): mla_prefill_ragged_kvsplit without the workspace
+ * arguments.  The key split's partial rows and log-sum-exps go to a device array
+ * of the library (MLA_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the
+ * process ends; its address is looked up once per GPU, on the first split call
+ * there).  The call allocates nothing and calls no allocating routine; debug
+ * mode does not apply to it.  Nothing in the array has to start at zero (each
+ * split tile's two halves write their partials before the merge reads them).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: two split calls whose work may overlap in time on one GPU (other
+ * streams, or graphs replayed concurrently) race and must not be issued.
+ * Outputs are those of mla_prefill_ragged_kvsplit with the same split_keys.
+ * Errors: as mla_prefill_ragged_kvsplit; BAD_SHAPE also for a split call
+ * (split_keys != 0) whose partials exceed MLA_NOALLOC_SCRATCH_BYTES.
+ */
+mla_status_t mla_prefill_ragged_kvsplit_noalloc(void* output, mla_dtype_t output_dtype, float* lse, const void* q,
+                                                mla_dtype_t qkv_dtype, const void* k_nope, const void* v,
+                                                const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                                const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                                const uint32_t* cache_offsets, uint32_t batch_size,
+                                                uint32_t total_q_tokens, uint32_t num_heads, uint32_t q_depth,
+                                                uint32_t depth, mla_mask_t mask, float scale, const float* q_scale,
+                                                const float* k_nope_scale, const float* v_scale,
+                                                uint32_t q_max_seq_len, uint32_t split_keys, void* stream);
+
 /*
  * mla_prefill_ragged_row -- one buffer row of the plan of page
  * "generic_flare_mla_prefill_ragged_paged_plan" (description, Args: rows of

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     mla_prefill_ragged,
     mla_prefill_ragged_krope,
     mla_prefill_ragged_kvsplit,
+    mla_prefill_ragged_kvsplit_noalloc,
     mla_prefill_ragged_lse,
     mla_prefill_ragged_row,
     mla_prefill_ragged_split,

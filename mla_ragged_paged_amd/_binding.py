@@ -83,6 +83,9 @@ def _load():
                                                u32, i32, ctypes.c_float, vp, vp, vp, u32, u32, vp, ctypes.c_uint64,
                                                vp]
     lib.mla_prefill_ragged_kvsplit.restype = i32
+    lib.mla_prefill_ragged_kvsplit_noalloc.argtypes = [vp, i32, vp, vp, i32, vp, vp, cp, u32, vp, vp, vp, u32, u32,
+                                                       u32, u32, u32, i32, ctypes.c_float, vp, vp, vp, u32, u32, vp]
+    lib.mla_prefill_ragged_kvsplit_noalloc.restype = i32
     lib.mla_prefill_kvsplit_workspace_bytes.argtypes = [u32, u32]
     lib.mla_prefill_kvsplit_workspace_bytes.restype = ctypes.c_uint64
     lib.mla_prefill_ragged_krope.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32, u32, u32, u32, u32,
@@ -337,6 +340,32 @@ def mla_prefill_ragged_kvsplit(output, q, k_nope, v, k_rope: PagedCache, layer_i
                                            _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), int(split_keys),
                                            _f32(workspace, "workspace"), nbytes, _stream(stream)),
            "mla_prefill_ragged_kvsplit")
+
+
+MLA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mla_prefill_ragged_kvsplit_noalloc(output, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length,
+                                       cache_row_offsets, cache_offsets, scale, split_keys, lse=None, q_scale=None,
+                                       k_nope_scale=None, v_scale=None, q_max_seq_len=0, stream=None,
+                                       mask="causal"):
+    """mla_prefill_ragged_kvsplit with the partials in the library's own device array
+    (MLA_NOALLOC_SCRATCH_BYTES per GPU): no workspace, nothing allocated.  Split calls
+    that may overlap in time on one GPU race."""
+    T, H, qd = q.shape
+    _contiguous(output=output, lse=lse, q=q, k_nope=k_nope, v=v)
+    _shapes(T, H, rows=[("output", output)], lses=[("lse", lse)])
+    _kv(H, q.dtype, k_nope, v)
+    s = k_rope.as_struct()
+    _check(_lib.mla_prefill_ragged_kvsplit_noalloc(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _ptr(q),
+                                                   _dtype_code(q), _ptr(k_nope), _ptr(v), ctypes.byref(s),
+                                                   layer_idx, _idx(valid_length, "valid_length"),
+                                                   _idx(cache_row_offsets, "cache_row_offsets"),
+                                                   _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1,
+                                                   T, H, qd, k_nope.shape[2], _mask_code(mask), float(scale),
+                                                   _ptr(q_scale), _ptr(k_nope_scale), _ptr(v_scale),
+                                                   int(q_max_seq_len), int(split_keys), _stream(stream)),
+           "mla_prefill_ragged_kvsplit_noalloc")
 
 
 def mla_prefill_ragged_row(output, acc, acc_lse, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length,

@@ -110,6 +110,38 @@ mla::CheckArgs check_args(const mla_paged_cache_t* kv, uint32_t batch) {
   return c;
 }
 
+// ---- scratch of mla_prefill_ragged_kvsplit_noalloc: the key split's fp32
+// partial rows and log-sum-exps, in a device array of this library (each GPU
+// the library runs on holds its own copy until the process ends).  Host code
+// uses the array only through the device address hipGetSymbolAddress gives for
+// each GPU, looked up on the first call on that GPU.
+static __device__ __align__(256) float scratch[MLA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[MAX_DEVICES] = {};
+
+hipError_t scratch_of_stream(hipStream_t s, float** out) {
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 const uint8_t* layer_base(const mla_paged_cache_t* kv, uint32_t layer_idx) {
   return static_cast<const uint8_t*>(kv->data) +
          (size_t)layer_idx * kv->num_pages * kv->page_size * kv->row_width * dtype_bytes(kv->dtype);
@@ -264,7 +296,8 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
                           const uint32_t* cache_offsets, uint32_t batch_size, uint32_t total_q_tokens,
                           uint32_t num_heads, uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
                           const float* q_scale, const float* k_nope_scale, const float* v_scale,
-                          uint32_t q_max_seq_len, void* stream, const KvSplit& kvs = KvSplit{0u, nullptr, 0u}) {
+                          uint32_t q_max_seq_len, void* stream, const KvSplit& kvs = KvSplit{0u, nullptr, 0u},
+                          bool debug_allowed = true) {
   if (!output || !qs.q || !k_nope || !v || !valid_length || !cache_row_offsets) return MLA_ERR_NULL_ARG;
   if (kvs.split_keys != 0) {
     if (!kvs.workspace) return MLA_ERR_NULL_ARG;
@@ -337,7 +370,7 @@ mla_status_t prefill_impl(void* output, mla_dtype_t output_dtype, float* lse, co
     c.q_max = q_max_seq_len;
     c.row_offsets = cache_row_offsets;
     c.row_positions = cache_offsets;
-    mla_status_t st = debug_check(c, stream);
+    mla_status_t st = debug_allowed ? debug_check(c, stream) : MLA_OK;
     if (st != MLA_OK) return st;
   }
   mla::PrefillArgs a{};
@@ -475,6 +508,36 @@ mla_status_t mla_prefill_ragged_kvsplit(void* output, mla_dtype_t output_dtype, 
                       valid_length, cache_row_offsets, cache_offsets, batch_size, total_q_tokens, num_heads, q_depth,
                       depth, mask, scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream,
                       KvSplit{split_keys, workspace, workspace_bytes});
+}
+
+mla_status_t mla_prefill_ragged_kvsplit_noalloc(void* output, mla_dtype_t output_dtype, float* lse, const void* q,
+                                                mla_dtype_t qkv_dtype, const void* k_nope, const void* v,
+                                                const mla_paged_cache_t* k_rope, uint32_t layer_idx,
+                                                const uint32_t* valid_length, const uint32_t* cache_row_offsets,
+                                                const uint32_t* cache_offsets, uint32_t batch_size,
+                                                uint32_t total_q_tokens, uint32_t num_heads, uint32_t q_depth,
+                                                uint32_t depth, mla_mask_t mask, float scale, const float* q_scale,
+                                                const float* k_nope_scale, const float* v_scale,
+                                                uint32_t q_max_seq_len, uint32_t split_keys, void* stream) {
+  // the partials of a split call must fit the scratch array (checked before the
+  // array's address is looked up, so a rejected call touches no GPU)
+  if (split_keys != 0 && (split_keys < 128 || mla_prefill_kvsplit_workspace_bytes(total_q_tokens, num_heads) >
+                                                  MLA_NOALLOC_SCRATCH_BYTES))
+    return MLA_ERR_BAD_SHAPE;
+  // an empty call launches nothing and needs no scratch
+  const bool split = split_keys != 0 && batch_size != 0 && total_q_tokens != 0 && num_heads != 0;
+  float* ws = nullptr;
+  if (split) {
+    if (g_fail_launch != 0) return hip_status(static_cast<hipError_t>(g_fail_launch));
+    const hipError_t e = scratch_of_stream(static_cast<hipStream_t>(stream), &ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  // no debug check: it would allocate its flag and synchronise
+  return prefill_impl(output, output_dtype, lse, nullptr, nullptr, nullptr, nullptr, false,
+                      QuerySource{q, nullptr, nullptr, false}, qkv_dtype, k_nope, v, k_rope, layer_idx,
+                      valid_length, cache_row_offsets, cache_offsets, batch_size, total_q_tokens, num_heads, q_depth,
+                      depth, mask, scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream,
+                      KvSplit{split ? split_keys : 0u, ws, MLA_NOALLOC_SCRATCH_BYTES}, false);
 }
 
 uint64_t mla_prefill_kvsplit_workspace_bytes(uint32_t total_q_tokens, uint32_t num_heads) {

@@ -31,8 +31,9 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["mla_prefill_check", "mla_prefill_gather", "mla_prefill_kvsplit_workspace_bytes",
                                     "mla_prefill_last_hip_error", "mla_prefill_latent_up", "mla_prefill_merge",
                                     "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_krope",
-                                    "mla_prefill_ragged_kvsplit", "mla_prefill_ragged_lse", "mla_prefill_ragged_row",
-                                    "mla_prefill_ragged_split", "mla_prefill_set_debug", "mla_status_string"]
+                                    "mla_prefill_ragged_kvsplit", "mla_prefill_ragged_kvsplit_noalloc",
+                                    "mla_prefill_ragged_lse", "mla_prefill_ragged_row", "mla_prefill_ragged_split",
+                                    "mla_prefill_set_debug", "mla_status_string"]
 
 
 def test_binding_exposes_every_entry_point():
@@ -323,3 +324,21 @@ def test_krope_validation_without_gpu():
     assert lib.mla_prefill_ragged_krope(*args(rows=ctypes.c_void_p(264))) == 2   # rows not 16-byte aligned
     assert lib.mla_prefill_ragged_krope(*args(out=None)) == 1
     assert lib.mla_prefill_ragged_krope(*args(b=0)) == 0                      # empty batch: a no-op
+
+
+def test_kvsplit_noalloc_validation_without_gpu():
+    """mla_prefill_ragged_kvsplit_noalloc: size and argument checks return before any HIP call."""
+    import mla_ragged_paged_amd._binding as b
+    lib = b._lib
+    d = ctypes.c_void_p(256)
+    s = b._Cache(data=256, dtype=0, num_layers=1, num_pages=1, page_size=16, row_width=64, rope_col=0,
+                 page_table=256, max_pages_per_seq=1, cache_lengths=256, scale=None)
+    ref = ctypes.byref(s)
+
+    def args(**kw):
+        return [kw.get("out", d), 0, None, d, 0, d, d, ref, 0, d, d, None, kw.get("b", 1), kw.get("t", 4),
+                kw.get("h", 2), 192, 128, 0, ctypes.c_float(0.07), None, None, None, 0, kw.get("sk", 256), None]
+    assert lib.mla_prefill_ragged_kvsplit_noalloc(*args(t=16257, h=4)) == 2      # partials past 64 MiB
+    assert lib.mla_prefill_ragged_kvsplit_noalloc(*args(sk=64)) == 2              # split_keys below 128
+    assert lib.mla_prefill_ragged_kvsplit_noalloc(*args(out=None, sk=0)) == 1
+    assert lib.mla_prefill_ragged_kvsplit_noalloc(*args(b=0)) == 0                # empty batch: a no-op
