@@ -10,22 +10,34 @@
 // slot g holds, and W [H*256][latent_dim] bf16.
 //
 // A dense contraction, so it runs on the 32x32x16 bf16 MFMA: C^T = W . L^T with
-// W rows as the A operand and the gathered latent rows as B.  A workgroup of
-// eight waves owns 256 output features (one head: its 128 key rows and 128
-// value rows) x 256 buffer slots, so every weight and latent row it stages
-// serves 256 outputs and the L2 -> LDS traffic is 1/128 byte per FLOP (a
-// 128 x 128 tile, measured at 15-20 % lower throughput, moves twice that).  Each wave owns
-// 128 features x 64 slots (4 x 2 MFMA tiles, 128 accumulator VGPRs).  The
-// reduction runs in chunks of 64 latent columns through two LDS stages of
-// 64 KB (weights 32 KB, latent 32 KB), filled by direct-to-LDS buffer loads:
-// weight rows by plain offsets, latent rows through the page table (each lane
-// resolves its four slots' cache rows once, from the plan row kept in LDS).
-// 16-byte chunks are XOR-swizzled by (row / 2) % 8, which keeps the operand
-// reads free of bank conflicts; operand fragments are read one k-step ahead of
-// their MFMAs.  The epilogue rounds to bf16, transposes through LDS and writes
-// whole 256-byte rows of K_nope and V.
+// W rows as the A operand and the gathered latent rows as B.  A tile is 256
+// output features (one head: its 128 key rows and 128 value rows) x 256 buffer
+// slots, so every weight and latent row staged serves 256 outputs and the
+// L2 -> LDS traffic is 1/128 byte per FLOP (a 128 x 128 tile, measured at 15-20 %
+// lower throughput, moves twice that).  A workgroup of eight waves computes one
+// tile at a time; each wave owns 128 features x 64 slots (4 x 2 MFMA tiles, 128
+// accumulator VGPRs).  The reduction runs in chunks of 64 latent columns through
+// two LDS stages of 64 KB (weights 32 KB, latent 32 KB), filled by
+// direct-to-LDS buffer loads: weight rows by plain offsets, latent rows through
+// the page table (each lane resolves its four slots' cache rows from the plan
+// row, which stays in LDS for the whole launch).  16-byte chunks are
+// XOR-swizzled by (row / 2) % 8, which keeps the operand reads free of bank
+// conflicts; operand fragments are read one k-step ahead of their MFMAs.
+//
+// The grid is persistent: one workgroup per CU (the 160 KB of LDS allow no
+// more) takes its XCD's tiles in turn.  The next tile's latent rows are looked
+// up while the current tile's first chunk runs, and its first chunk is loaded
+// as soon as the epilogue has handed the stage memory back, so a tile starts
+// without a cold page-table lookup or a workgroup launch.  The epilogue rounds
+// to bf16, transposes through LDS and writes whole 256-byte rows of K_nope and V
+// with streaming (non-temporal) stores: the rows are not read again by this
+// kernel, and keeping them out of L2 leaves it to the weight and latent rows
+// (measured 13-15 % faster than plain stores on the 16K-token and prefix rows).
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
+#include "mla_prefill.h"
 
 namespace mla {
 namespace {
@@ -38,6 +50,7 @@ constexpr int A_OFF = 0;              // W tile      [256 rows][8 chunks of 16 B
 constexpr int B_OFF = TF * KC * 2;    // latent tile [256 rows][8 chunks]          32 KiB
 constexpr int LSTAGE = (TF + TS) * KC * 2;   // 64 KiB
 constexpr int LLDS = 2 * LSTAGE;             // 128 KiB
+constexpr int PLAN_BYTES = 4 * MLA_MAX_BATCH;       // plan row entries [0, batch): 32 KiB
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
@@ -52,22 +65,28 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __global__ void __launch_bounds__(NTH, 1) latent_up_kernel(LatentArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LLDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LLDS + PLAN_BYTES];
+  uint32_t* sbro = reinterpret_cast<uint32_t*>(lds + LLDS);    // plan row, entries [0, batch)
 
-  // ---- tile.  XCD x (workgroup id % 8) takes a contiguous eighth of the heads.
-  // Within it, tiles run in blocks of up to 8 heads x 8 slot tiles (head
-  // fastest), so the 32 workgroups an XCD runs at once share 2 MB of weight rows
-  // and 2 MB of latent rows, both held by its 4 MB L2.
-  const uint32_t nt = a.heads;                     // feature tiles: one per head
-  const uint32_t mtn = (a.cap + TS - 1) / TS;      // slot tiles
-  const uint32_t bid = blockIdx.x;
-  uint32_t ft, mt;
-  {
-    const bool split8 = (nt & 7u) == 0;
-    const uint32_t per = split8 ? nt >> 3 : nt;
-    const uint32_t f_base = split8 ? (bid & 7u) * per : 0u;
-    const uint32_t j = split8 ? bid >> 3 : bid;
-    const uint32_t gf = min(per, 8u), gm = 8u;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int li = lane & 31, hf = lane >> 5;
+
+  // ---- this workgroup's tiles.  With H a multiple of 8, XCD x (workgroup id % 8)
+  // owns the tiles of heads [x*H/8, (x+1)*H/8) and its workgroups take that list
+  // round-robin; the list runs in blocks of up to 4 heads x 8 slot tiles (head
+  // fastest), so the 32 tiles an XCD runs at once share 1 MB of weight rows and
+  // 2 MB of latent rows, both held by its 4 MB L2 (blocks of 8 heads, 4 MB in
+  // all, measured 1-2 % slower).
+  const uint32_t used = min(a.bro[a.batch], a.cap);   // slots this plan row fills
+  const uint32_t mtn = (used + TS - 1) / TS;       // slot tiles holding a used slot
+  const bool split8 = (a.heads & 7u) == 0;
+  const uint32_t per = split8 ? a.heads >> 3 : a.heads;
+  const uint32_t f_base = split8 ? (blockIdx.x & 7u) * per : 0u;
+  const uint32_t wgs = split8 ? gridDim.x >> 3 : gridDim.x;
+  const uint32_t ntiles = per * mtn;
+  auto tile_of = [&](uint32_t j, uint32_t& ft, uint32_t& mt) {
+    const uint32_t gf = min(per, 4u), gm = 8u;
     const uint32_t mg = j / (per * gm);
     const uint32_t r = j - mg * per * gm;
     const uint32_t gml = min(gm, mtn - mg * gm);
@@ -76,55 +95,49 @@ __global__ void __launch_bounds__(NTH, 1) latent_up_kernel(LatentArgs a) {
     const uint32_t q = r - fg * gf * gml;
     ft = f_base + fg * gf + q % gfl;
     mt = mg * gm + q / gfl;
-  }
-  const uint32_t used = a.bro[a.batch];            // slots this plan row fills
-  const uint32_t m0 = mt * TS;
-  if (m0 >= used) return;
+  };
+  uint32_t j = split8 ? blockIdx.x >> 3 : blockIdx.x;
+  if (j >= ntiles) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int li = lane & 31, hf = lane >> 5;
-
-  // ---- the plan row in LDS, then each lane's four latent rows (slot
-  // m0 + 32w + 8u + lane/8 for load u) as byte offsets into the cache layer
-  uint32_t* sbro = reinterpret_cast<uint32_t*>(lds);
-  for (uint32_t i = tid; i <= a.batch; i += NTH) sbro[i] = a.bro[i];
+  for (uint32_t i = tid; i < a.batch; i += NTH) sbro[i] = a.bro[i];
   __syncthreads();
-  uint32_t row_off[4];
+
+  // each lane's four latent rows of slot tile mt (slot 32w + 8u + lane/8 for
+  // load u) as byte offsets into the cache layer; the source chunk is folded in
+  auto rows_of = [&](uint32_t mt, uint32_t (&src)[4]) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint32_t g = m0 + 32 * w + 8 * u + (lane >> 3);
-    row_off[u] = a.cache_bytes;                     // past the end: the load returns zeros
-    if (g < used && g >= sbro[0]) {
-      uint32_t lo = 0, hi = a.batch;                // last b with sbro[b] <= g, b < batch
-      while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (sbro[mid] <= g) lo = mid; else hi = mid;
+    for (int u = 0; u < 4; ++u) {
+      const int r = 32 * w + 8 * u + (lane >> 3);
+      const uint32_t g = mt * TS + (uint32_t)r;
+      uint32_t off = a.cache_bytes;                 // past the end: the load returns zeros
+      if (g < used && g >= sbro[0]) {
+        uint32_t lo = 0, hi = a.batch;              // last b with sbro[b] <= g, b < batch
+        while (hi - lo > 1) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (sbro[mid] <= g) lo = mid; else hi = mid;
+        }
+        const uint32_t pos = a.co[lo] + (g - sbro[lo]);
+        const uint32_t* pt = a.page_table + (size_t)lo * a.max_pages;
+        const uint32_t page = a.page_shift < 32u ? pt[pos >> a.page_shift] : pt[pos / a.page_size];
+        const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
+        off = (page * a.page_size + slot) * a.row_bytes + a.latent_col * 2;
       }
-      const uint32_t pos = a.co[lo] + (g - sbro[lo]);
-      const uint32_t* pt = a.page_table + (size_t)lo * a.max_pages;
-      const uint32_t page = a.page_shift < 32u ? pt[pos >> a.page_shift] : pt[pos / a.page_size];
-      const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
-      row_off[u] = (page * a.page_size + slot) * a.row_bytes + a.latent_col * 2;
+      src[u] = off + 16u * (uint32_t)((lane & 7) ^ swz(r));
     }
-  }
-  __syncthreads();                                  // the plan row's LDS is reused below
+  };
 
   // ---- load slots: load u of wave w covers tile rows 32w + 8u .. +7; lane ->
   // row 32w + 8u + lane/8, stored chunk lane%8 holds source chunk (lane%8) ^ swz(row)
-  const uint32_t n0 = ft * TF;
   const uint32_t kdim = a.latent_dim;
-  const auto w_rs = rsrc(a.w + (size_t)n0 * kdim, TF * kdim * 2);
   const auto c_rs = rsrc(a.cache, a.cache_bytes);
-  uint32_t a_off[4], b_src[4];
+  uint32_t a_off[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 32 * w + 8 * u + (lane >> 3);
-    const uint32_t cs = (uint32_t)((lane & 7) ^ swz(r));
-    a_off[u] = (uint32_t)r * kdim * 2 + 16u * cs;
-    b_src[u] = row_off[u] + 16u * cs;
+    a_off[u] = (uint32_t)r * kdim * 2 + 16u * (uint32_t)((lane & 7) ^ swz(r));
   }
-  auto issue = [&](uint32_t kc, int stage) {
+  auto w_rsrc = [&](uint32_t ft) { return rsrc(a.w + (size_t)ft * TF * kdim, TF * kdim * 2); };
+  auto issue = [&](__amdgpu_buffer_rsrc_t w_rs, const uint32_t (&b_src)[4], uint32_t kc, int stage) {
     MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)lds + stage * LSTAGE;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -152,83 +165,117 @@ __global__ void __launch_bounds__(NTH, 1) latent_up_kernel(LatentArgs a) {
     for (int ks = 0; ks < 4; ++ks) b_rd[y][ks] = B_OFF + rb * 128 + 16 * ((2 * ks + hf) ^ swz(rb));
   }
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
-
+  // ---- tiles in turn.  Each tile's chunks go through stages 0, 1, 0, ...; the
+  // next tile's latent rows are looked up while the first chunk runs.
   const uint32_t nkc = kdim / KC;
-  issue(0, 0);
-  for (uint32_t kc = 0; kc < nkc; ++kc) {
-    const int stage = kc & 1;
-    // publish chunk kc (every wave's loads done) and retire the other stage
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kc + 1 < nkc) issue(kc + 1, stage ^ 1);
-    const uint8_t* st = lds + stage * LSTAGE;
-    // fragments of k-step ks + 1 are read while the MFMAs of ks run
-    bf16x8 fa[2][4], fb[2][2];
-    auto rd = [&](int ks, int slot) {
+  uint32_t ft, mt;
+  tile_of(j, ft, mt);
+  uint32_t b_src[4];
+  rows_of(mt, b_src);
+  auto w_rs = w_rsrc(ft);
+  issue(w_rs, b_src, 0, 0);
+  int stage = 0;
+  const size_t row_stride = (size_t)a.heads * 128;
+  while (true) {
+    const uint32_t jn = j + wgs;
+    const bool more = jn < ntiles;
+    uint32_t ftn = 0, mtn_ = 0;
+    uint32_t b_next[4] = {0u, 0u, 0u, 0u};
+    f32x16 acc[4][2];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) fa[slot][x] = *reinterpret_cast<const bf16x8*>(st + a_rd[x][ks]);
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int y = 0; y < 2; ++y) fb[slot][y] = *reinterpret_cast<const bf16x8*>(st + b_rd[y][ks]);
-    };
-    rd(0, 0);
+      for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+    for (uint32_t kc = 0; kc < nkc; ++kc) {
+      // publish chunk kc (every wave's loads done) and retire the other stage
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kc == 0 && more) {
+        tile_of(jn, ftn, mtn_);
+        rows_of(mtn_, b_next);
+      }
+      if (kc + 1 < nkc) issue(w_rs, b_src, kc + 1, stage ^ 1);
+      const uint8_t* st = lds + stage * LSTAGE;
+      // fragments of k-step ks + 1 are read while the MFMAs of ks run
+      bf16x8 fa[2][4], fb[2][2];
+      auto rd = [&](int ks, int slot) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) rd(ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int x = 0; x < 4; ++x) fa[slot][x] = *reinterpret_cast<const bf16x8*>(st + a_rd[x][ks]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+        for (int y = 0; y < 2; ++y) fb[slot][y] = *reinterpret_cast<const bf16x8*>(st + b_rd[y][ks]);
+      };
+      rd(0, 0);
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(fa[ks & 1][x], fb[ks & 1][y], acc[x][y]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) rd(ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(fa[ks & 1][x], fb[ks & 1][y], acc[x][y]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stage ^= 1;
     }
-  }
 
-  // ---- epilogue: acc[x][y][i] is feature 128wn + 32x + 8(i/4) + 4hf + i%4 of
-  // slot 64wm + 32y + li.  Round to bf16 and write the tile as [slot][feature]
-  // (512 B per slot: key 256 B then value 256 B; 16-byte chunk c at c ^ (slot % 32)),
-  // then store whole rows.
-  __syncthreads();                                  // every wave is done reading the stages
+    // ---- epilogue: acc[x][y][i] is feature 128wn + 32x + 8(i/4) + 4hf + i%4 of
+    // slot 64wm + 32y + li.  Round to bf16 and write the tile as [slot][feature]
+    // (512 B per slot: key 256 B then value 256 B; 16-byte chunk c at c ^ (slot % 32))
+    // through the stage memory, take each thread's 16 row chunks back into
+    // registers, hand the memory to the next tile's first loads, then store whole
+    // rows (streaming stores: the rows are not read again here).
+    __syncthreads();                                // every wave is done reading the stages
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int r = 64 * wm + 32 * y + li;
+      for (int y = 0; y < 2; ++y) {
+        const int r = 64 * wm + 32 * y + li;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = 128 * wn + 32 * x + 8 * q + 4 * hf;
-        const uint32_t w0 = pack_bf16x2(acc[x][y][4 * q], acc[x][y][4 * q + 1]);
-        const uint32_t w1 = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
-        const int chunk = (f >> 3) ^ (r & 31);
-        *reinterpret_cast<MLA_LDS u32x2*>((MLA_LDS uint8_t*)lds + r * 512 + 16 * chunk + 2 * (f & 7)) =
-            u32x2{w0, w1};
+        for (int q = 0; q < 4; ++q) {
+          const int f = 128 * wn + 32 * x + 8 * q + 4 * hf;
+          const uint32_t w0 = pack_bf16x2(acc[x][y][4 * q], acc[x][y][4 * q + 1]);
+          const uint32_t w1 = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
+          const int chunk = (f >> 3) ^ (r & 31);
+          *reinterpret_cast<MLA_LDS u32x2*>((MLA_LDS uint8_t*)lds + r * 512 + 16 * chunk + 2 * (f & 7)) =
+              u32x2{w0, w1};
+        }
+      }
+    __syncthreads();
+    i32x4 rowv[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int r = 16 * it + (tid >> 5), cc = tid & 31;
+      rowv[it] = *reinterpret_cast<const MLA_LDS i32x4*>((MLA_LDS uint8_t*)lds + r * 512 + 16 * (cc ^ (r & 31)));
+    }
+    __syncthreads();                                // the stage memory is free again
+    if (more) issue(w_rsrc(ftn), b_next, 0, 0);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int r = 16 * it + (tid >> 5), cc = tid & 31;
+      const uint32_t g = mt * TS + r;
+      if (g < used) {
+        uint16_t* dst = (cc < 16 ? a.k_nope : a.v) + g * row_stride + ft * 128 + (cc & 15) * 8;
+        __builtin_nontemporal_store(rowv[it], reinterpret_cast<i32x4*>(dst));
       }
     }
-  __syncthreads();
-  const uint32_t head = ft;
-  const size_t row_stride = (size_t)a.heads * 128;
+    if (!more) break;
+    stage = 0;
+    j = jn;
+    ft = ftn;
+    mt = mtn_;
+    w_rs = w_rsrc(ft);
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int r = 16 * it + (tid >> 5), c = tid & 31;    // 32 chunks per slot: 16 key + 16 value
-    const uint32_t g = m0 + r;
-    if (g < used) {
-      const i32x4 val = *reinterpret_cast<const MLA_LDS i32x4*>((MLA_LDS uint8_t*)lds + r * 512 + 16 * (c ^ (r & 31)));
-      uint16_t* dst = (c < 16 ? a.k_nope : a.v) + g * row_stride + head * 128 + (c & 15) * 8;
-      st16(dst, val);
-    }
+    for (int u = 0; u < 4; ++u) b_src[u] = b_next[u];
   }
 }
 
 }  // namespace
 
 hipError_t launch_latent_up(const LatentArgs& a, hipStream_t stream) {
-  const uint64_t mt = (a.cap + TS - 1) / TS;
-  const uint64_t grid = mt * a.heads;
-  if (grid == 0) return hipSuccess;
+  // one workgroup per CU at most (256 CUs, 32 per XCD), each taking tiles in turn
+  const uint64_t tiles = (uint64_t)(a.cap + TS - 1) / TS * a.heads;
+  if (tiles == 0) return hipSuccess;
+  const uint64_t grid = (a.heads & 7u) == 0 ? 8u * std::min<uint64_t>(32u, tiles / 8u) : std::min<uint64_t>(256u, tiles);
   hipLaunchKernelGGL(latent_up_kernel, dim3((uint32_t)grid), dim3(NTH), 0, stream, a);
   return hipGetLastError();
 }

@@ -284,8 +284,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     pg_next[1] = page_of(kt_lo + 1, 1);
     // all four waves start their first tile together.  (Measured on the single
     // 16K-token sequence: how far apart the workgroups' K/V streams run, and so
-    // the L2 hit rate, depends on this start-up; this form gives 7x algorithmic
-    // HBM traffic where others gave up to 19x.)
+    // the L2 hit rate, depends on this start-up; this form gives about 6x the
+    // algorithmic HBM traffic where others gave up to 19x.)
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     issue_kv(kt_lo, (MLA_LDS uint8_t*)lds + (kt_lo & 1) * STAGE);
@@ -293,13 +293,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     load_q();
     __builtin_amdgcn_sched_barrier(0);
     issue_rope(kt_lo, (MLA_LDS uint8_t*)lds + (kt_lo & 1) * STAGE, pg0);
-  } else {
-    // With no key to attend to, Q is never read (the epilogue writes 0 or passes
-    // an earlier partial through).  The load stays: without this branch the
-    // compiled layout of the kernel changes and the single 16K-token sequence
-    // fell into the start-up regime with ~3x the HBM traffic (measured).
-    load_q();
   }
+  // with no key to attend to, Q is never read (the epilogue writes 0, or passes
+  // an earlier partial through)
 
   for (int32_t kt = kt_lo; kt < kt_hi; ++kt) {
     const int stage = kt & 1;
@@ -346,6 +342,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       };
       kread(0, kf[0]);
       kread(1, kf[1]);
+      // The MFMA sections run at raised wave priority, so the other workgroup's
+      // wave on this SIMD (in its softmax) yields the issue slot to MFMA issue.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks) {
         if (ks + 2 < 12) kread(ks + 2, kf[(ks + 2) % 3]);
@@ -354,6 +353,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         for (int kb = 0; kb < KB; ++kb) s[kb] = mfma_bf16(kf[ks % 3][kb], qop[ks], s[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // s[kb][r] is key j0 + 32kb + 4hf + roff(r), roff(r) = 8(r/4) + r%4
       const bool full = (j0 + BN <= len) && (!causal || c0 + j0 + BN - 1 <= wq_first);
       if (!full) {
@@ -415,6 +415,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       }
 
       // O^T += V^T P^T, four (two) 16-key steps; V fragments are read one step ahead
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < 2 * KB; ++kk) {
         const i32x4 pv = {(int)pw[4 * kk], (int)pw[4 * kk + 1], (int)pw[4 * kk + 2], (int)pw[4 * kk + 3]};
@@ -425,6 +426,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         for (int d = 0; d < 4; ++d) o[d] = mfma_bf16(vf[kk & 1][d], pop, o[d]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     if (wave_rows && (!causal || c0 + j0 <= wq_last)) {
       if (half_tile)
