@@ -43,8 +43,9 @@
  *                           log-sum-exp, optionally merged in place with the
  *                           partial result of earlier rows;
  *   mla_prefill_ragged_row  one row of such a plan, rows run in order: each
- *                           sequence's partial is carried in an fp32 accumulator
- *                           from its first row to its last, which writes the output;
+ *                           token's partial is carried in an fp32 accumulator
+ *                           from its sequence's first row to the row holding its
+ *                           last visible key, which writes the output;
  *   mla_prefill_merge       log-sum-exp combine of two partial results.
  *
  * Conventions for every call:
@@ -488,19 +489,25 @@ mla_status_t mla_prefill_ragged_kvsplit_noalloc(void* output, mla_dtype_t output
  * plan (its buffer_row_offsets[r] and cache_offsets[r]) and k_nope / v that
  * row's K/V buffer.  The call is made once per row, r = 0, 1, ..., in order on
  * one stream, with the same acc / acc_lse for every row of the batch.  For a
- * sequence b whose slice in this row is not empty, with len_b keys starting at
- * cache position c_b = cache_offsets[b]:
- *   c_b == 0 (b's first row)        the row's partial (output and lse as in
+ * query token i of sequence b whose slice in this row is not empty, with len_b
+ * keys starting at cache position c_b = cache_offsets[b], and k_i the cache
+ * position of the token's last visible key (p_b + i under the causal mask,
+ * p_b + n_b - 1 under the null mask; p_b = kv->cache_lengths[b]):
+ *   k_i < c_b                       the row holds none of its keys: not touched;
+ *   c_b == 0 (first row), k_i >= len_b
+ *                                   the row's partial (output and lse as in
  *                                   mla_prefill_ragged_lse) goes to acc / acc_lse;
- *   neither first nor last          the row's partial is merged into acc / acc_lse;
- *   c_b + len_b == kv->cache_lengths[b] + n_b (b's last row)
+ *   c_b > 0, k_i >= c_b + len_b     the row's partial is merged into acc / acc_lse;
+ *   c_b > 0, c_b <= k_i < c_b + len_b (the row holding its last key)
  *                                   the row's partial is merged with acc / acc_lse
  *                                   and the result goes to output (and lse);
- *   first and last                  the row's result goes straight to output (and lse).
- * A sequence with no keys in this row is not touched.  After the last row,
- * output holds the attention over every key of every sequence (what
- * mla_prefill_ragged computes over one row holding all of them), and lse, when
- * given, its log-sum-exp.
+ *   c_b == 0, k_i < len_b           the row's result goes straight to output (and lse).
+ * So each token is finished by the row holding its last visible key, and later
+ * rows leave it alone (under the causal mask the tokens of a sequence finish in
+ * different rows).  acc / acc_lse hold no defined values for finished tokens.
+ * After the last row, output holds the attention over every key of every
+ * sequence (what mla_prefill_ragged computes over one row holding all of them),
+ * and lse, when given, its log-sum-exp.
  *
  *   output      device [total_q_tokens][num_heads][128], MLA_BF16 or MLA_FP32.
  *   lse         device fp32 [total_q_tokens][num_heads] or NULL.

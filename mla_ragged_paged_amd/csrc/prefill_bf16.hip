@@ -105,13 +105,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const uint32_t g0 = a.cache_row_offsets[b];
   const int32_t len = (int32_t)(a.cache_row_offsets[b + 1] - g0);
   const int32_t c0 = a.cache_offsets ? (int32_t)a.cache_offsets[b] : 0;
-  // row mode: a row holding none of the sequence's keys leaves its outputs alone
-  bool row_first = true, row_last = true;
+  // row mode: a row holding none of the sequence's keys leaves its outputs alone;
+  // row_first: this row's slice starts at cache position 0 (no earlier partial)
+  bool row_first = true;
   if constexpr (!PLAIN) {
     if (a.row_mode) {
       if (len == 0) return;
       row_first = c0 == 0;
-      row_last = c0 + len == p + (int32_t)n;
     }
   }
   const int32_t i_last = (int32_t)min(n, i0 + BM) - 1;
@@ -441,7 +441,52 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   // ---- epilogue: combine the two halves' row sums, normalise, store the row
   // with its log-sum-exp (merged with an earlier partial when one is given)
   const float l_tot = l_run + swap_halves(l_run);
-  if (my_i < (int32_t)n) {
+  if constexpr (PLAIN && !KVSPLIT) {
+    // Plain bf16 rows go through LDS (the stages are free once every wave is past
+    // its last tile): row 32w + li of the tile, 16-byte chunk c at c ^ (row % 16).
+    // Then 16 lanes store each query's whole 256-byte row with streaming stores,
+    // which keep the output out of L2 (K/V tiles of other units are read there).
+    // Storing the same 16-byte pieces straight from the registers with streaming
+    // stores measured 1.7x slower on dsv3; this form measured 0.5-2 % faster than
+    // plain stores from the registers.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __syncthreads();
+    MLA_LDS uint8_t* ot = (MLA_LDS uint8_t*)lds;
+    const int row = 32 * w + li;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t w0 = pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
+        *reinterpret_cast<MLA_LDS u32x2*>(ot + row * 256 + 16 * ((4 * d + g) ^ (row & 15)) + 8 * hf) =
+            u32x2{w0, w1};
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = 16 * it + (tid >> 4), cc = tid & 15;
+      if ((int32_t)i0 + r < (int32_t)n) {
+        const i32x4 v = *reinterpret_cast<const MLA_LDS i32x4*>(ot + r * 256 + 16 * (cc ^ (r & 15)));
+        __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(static_cast<uint16_t*>(a.out) +
+                                                                 ((size_t)(t0 + i0 + r) * H + h) * 128 + 8 * cc));
+      }
+    }
+    return;
+  }
+  // Row mode, per query: the row holding the query's last visible key (p + i under
+  // the causal mask, the context's last under the null mask) finishes it and
+  // writes the output; earlier rows carry its partial, and later rows -- which
+  // hold none of its keys -- leave it alone.
+  bool row_last = true, row_skip = false;
+  if constexpr (!PLAIN) {
+    if (a.row_mode) {
+      const int32_t k_last = causal ? p + my_i : p + (int32_t)n - 1;
+      row_skip = k_last < c0;
+      row_last = k_last < c0 + len;
+    }
+  }
+  if (my_i < (int32_t)n && !row_skip) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
     if (KVSPLIT && part)

@@ -110,13 +110,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   const uint32_t g0 = a.cache_row_offsets[b];
   const int32_t len = (int32_t)(a.cache_row_offsets[b + 1] - g0);
   const int32_t c0 = a.cache_offsets ? (int32_t)a.cache_offsets[b] : 0;
-  // row mode: a row holding none of the sequence's keys leaves its outputs alone
-  bool row_first = true, row_last = true;
+  // row mode: a row holding none of the sequence's keys leaves its outputs alone;
+  // row_first: this row's slice starts at cache position 0 (no earlier partial)
+  bool row_first = true;
   if constexpr (!PLAIN) {
     if (a.row_mode) {
       if (len == 0) return;
       row_first = c0 == 0;
-      row_last = c0 + len == p + (int32_t)n;
     }
   }
   const int32_t i_last = (int32_t)min(n, i0 + BM) - 1;
@@ -508,7 +508,19 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   // ---- epilogue: row sums of both halves, normalise (applying s_v), store the
   // row with its log-sum-exp (merged with an earlier partial when one is given)
   const float l_tot = l_run + swap_halves(l_run) + (MFMA_ROWSUM ? lsum[0] : 0.f);
-  if (my_i < (int32_t)n) {
+  // Row mode, per query: the row holding the query's last visible key (p + i under
+  // the causal mask, the context's last under the null mask) finishes it and
+  // writes the output; earlier rows carry its partial, and later rows -- which
+  // hold none of its keys -- leave it alone.
+  bool row_last = true, row_skip = false;
+  if constexpr (!PLAIN) {
+    if (a.row_mode) {
+      const int32_t k_last = causal ? p + my_i : p + (int32_t)n - 1;
+      row_skip = k_last < c0;
+      row_last = k_last < c0 + len;
+    }
+  }
+  if (my_i < (int32_t)n && !row_skip) {
     const float inv = l_tot > 0.f ? s_v / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? mc + __builtin_amdgcn_logf(l_tot) : -INFINITY;
     if (KVSPLIT && part)

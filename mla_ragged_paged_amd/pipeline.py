@@ -181,8 +181,9 @@ class PrefillStep:
 
     def attention_row_merged(self, row: int, stream=None):
         """Attention over plan row ``row`` of several (rows run in order): each
-        sequence's partial is carried in the fp32 accumulator from its first row
-        to its last, which writes the bf16 output."""
+        token's partial is carried in the fp32 accumulator from its sequence's
+        first row to the row holding its last visible key, which writes the bf16
+        output."""
         kn, v = self.row_buffers(row)
         sc = self.scales or {}
         B.mla_prefill_ragged_row(self.out, self.acc, self.lse, self.q, kn, v, self.kv, self.w.spec.layer_idx,
