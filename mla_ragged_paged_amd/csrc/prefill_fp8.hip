@@ -508,6 +508,39 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   // ---- epilogue: row sums of both halves, normalise (applying s_v), store the
   // row with its log-sum-exp (merged with an earlier partial when one is given)
   const float l_tot = l_run + swap_halves(l_run) + (MFMA_ROWSUM ? lsum[0] : 0.f);
+  if constexpr (PLAIN && !KVSPLIT) {
+    // Plain bf16 rows go through LDS (the stages are free once every wave is past
+    // its last tile): waves 0-1 (tile rows 0..63) in stage 0, waves 2-3 in stage
+    // 1, row r at (r % 64) * 256 with 16-byte chunk c at c ^ (r % 16).  Then 16
+    // lanes store each query's whole 256-byte row with streaming stores, which
+    // keep the output out of L2 (measured 1.5 % faster than plain stores from
+    // the registers).
+    const float inv = l_tot > 0.f ? s_v / l_tot : 0.f;
+    __syncthreads();
+    const int row = 32 * w + li;
+    MLA_LDS uint8_t* ot = (MLA_LDS uint8_t*)(row < 64 ? stage0 : stage1);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t w0 = pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv);
+        *reinterpret_cast<MLA_LDS u32x2*>(ot + (row & 63) * 256 + 16 * ((4 * d + g) ^ (row & 15)) + 8 * hf) =
+            u32x2{w0, w1};
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = 16 * it + (tid >> 4), cc = tid & 15;
+      const MLA_LDS uint8_t* src = (const MLA_LDS uint8_t*)(r < 64 ? stage0 : stage1);
+      if ((int32_t)i0 + r < (int32_t)n) {
+        const i32x4 v = *reinterpret_cast<const MLA_LDS i32x4*>(src + (r & 63) * 256 + 16 * (cc ^ (r & 15)));
+        __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(static_cast<uint16_t*>(a.out) +
+                                                                 ((size_t)(t0 + i0 + r) * H + h) * 128 + 8 * cc));
+      }
+    }
+    return;
+  }
   // Row mode, per query: the row holding the query's last visible key (p + i under
   // the causal mask, the context's last under the null mask) finishes it and
   // writes the output; earlier rows carry its partial, and later rows -- which
