@@ -282,11 +282,6 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     const uint32_t pg0[2] = {page_of(kt_lo, 0), page_of(kt_lo, 1)};
     pg_next[0] = page_of(kt_lo + 1, 0);
     pg_next[1] = page_of(kt_lo + 1, 1);
-    // all four waves start their first tile together.  (Measured on the single
-    // 16K-token sequence: how far apart the workgroups' K/V streams run, and so
-    // the L2 hit rate, depends on this start-up; this form gives about 6x the
-    // algorithmic HBM traffic where others gave up to 19x.)
-    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     issue_kv(kt_lo, (MLA_LDS uint8_t*)lds + (kt_lo & 1) * STAGE);
     __builtin_amdgcn_sched_barrier(0);
