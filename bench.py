@@ -261,6 +261,8 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
     step_med, _ = _median_ms(torch, mr.run, reps, stream)
 
     def rows_attention():
+        # attention launches only: the gathered K_rope rows then hold the last row's
+        # window for every row, which changes no work (the step time above is whole)
         for r in range(mr.rows):
             mr.attention_row_merged(r)
     attn_med, attn_best = _median_ms(torch, rows_attention, reps, stream)

@@ -46,6 +46,7 @@
  *                           token's partial is carried in an fp32 accumulator
  *                           from its sequence's first row to the row holding its
  *                           last visible key, which writes the output;
+ *   mla_prefill_ragged_row_krope  the same with K_rope as the row's gathered rows;
  *   mla_prefill_merge       log-sum-exp combine of two partial results.
  *
  * Conventions for every call:
@@ -526,6 +527,30 @@ mla_status_t mla_prefill_ragged_row(void* output, mla_dtype_t output_dtype, floa
                                     uint32_t depth, mla_mask_t mask, float scale, const float* q_scale,
                                     const float* k_nope_scale, const float* v_scale,
                                     uint32_t q_max_seq_len, void* stream);
+
+/*
+ * mla_prefill_ragged_row_krope -- mla_prefill_ragged_row with K_rope given as
+ * rows laid out like K (page "flare_mla_prefill", the overload whose k_rope is
+ * a tensor): for a row of the plan whose K_rope window has been gathered into
+ * contiguous rows (mla_prefill_gather of columns [rope_col, rope_col + 64)),
+ * so that the gather feeds the attention of every row of a multi-row plan.
+ *
+ *   k_rope, k_rope_scale, cache_lengths   as mla_prefill_ragged_krope: k_rope
+ *                   row cache_row_offsets[b] + j holds key j of sequence b's
+ *                   slice in this row.
+ * All other arguments, the per-token rule for acc / acc_lse / output, and the
+ * errors as mla_prefill_ragged_row.  The arithmetic is that call's, so with rows
+ * holding what the page table points at the outputs are the same bit for bit.
+ */
+mla_status_t mla_prefill_ragged_row_krope(void* output, mla_dtype_t output_dtype, float* lse, float* acc,
+                                          float* acc_lse, const void* q, mla_dtype_t qkv_dtype, const void* k_nope,
+                                          const void* v, const void* k_rope, const float* k_rope_scale,
+                                          const uint32_t* cache_lengths, const uint32_t* valid_length,
+                                          const uint32_t* cache_row_offsets, const uint32_t* cache_offsets,
+                                          uint32_t batch_size, uint32_t total_q_tokens, uint32_t num_heads,
+                                          uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
+                                          const float* q_scale, const float* k_nope_scale, const float* v_scale,
+                                          uint32_t q_max_seq_len, void* stream);
 
 /*
  * mla_prefill_merge -- combine two partial attention results over disjoint key

@@ -34,6 +34,7 @@ from ._binding import (  # noqa: F401
     mla_prefill_ragged_kvsplit_noalloc,
     mla_prefill_ragged_lse,
     mla_prefill_ragged_row,
+    mla_prefill_ragged_row_krope,
     mla_prefill_ragged_split,
     mla_prefill_set_debug,
     mla_status_string,

@@ -91,6 +91,9 @@ def _load():
     lib.mla_prefill_ragged_krope.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32, u32, u32, u32, u32,
                                              i32, ctypes.c_float, vp, vp, vp, u32, vp]
     lib.mla_prefill_ragged_krope.restype = i32
+    lib.mla_prefill_ragged_row_krope.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32, u32,
+                                                 u32, u32, u32, i32, ctypes.c_float, vp, vp, vp, u32, vp]
+    lib.mla_prefill_ragged_row_krope.restype = i32
     lib.mla_prefill_latent_up.argtypes = [cp, u32, u32, vp, vp, u32, u32, vp, u32, u32, vp, vp, vp]
     lib.mla_prefill_latent_up.restype = i32
     lib.mla_prefill_merge.argtypes = [vp, i32, vp, vp, vp, vp, vp, u32, u32, u32, vp]
@@ -371,8 +374,9 @@ def mla_prefill_ragged_kvsplit_noalloc(output, q, k_nope, v, k_rope: PagedCache,
 def mla_prefill_ragged_row(output, acc, acc_lse, q, k_nope, v, k_rope: PagedCache, layer_idx, valid_length,
                            cache_row_offsets, cache_offsets, scale, lse=None, q_scale=None, k_nope_scale=None,
                            v_scale=None, q_max_seq_len=0, stream=None, mask="causal"):
-    """One row of a multi-row plan (rows called in order): partials carried in acc fp32 [T, H, 128] /
-    acc_lse [T, H] from each sequence's first row to its last, which writes output (and lse)."""
+    """One row of a multi-row plan (rows called in order): each token's partial carried in acc fp32
+    [T, H, 128] / acc_lse [T, H] from its sequence's first row to the row holding its last visible
+    key, which writes output (and lse)."""
     T, H, qd = q.shape
     _contiguous(output=output, lse=lse, acc=acc, acc_lse=acc_lse, q=q, k_nope=k_nope, v=v)
     _shapes(T, H, rows=[("output", output), ("acc", acc)], lses=[("lse", lse), ("acc_lse", acc_lse)])
@@ -442,6 +446,28 @@ def mla_prefill_ragged_krope(output, q, k_nope, v, k_rope, cache_lengths, valid_
                                          k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
                                          _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
            "mla_prefill_ragged_krope")
+
+
+def mla_prefill_ragged_row_krope(output, acc, acc_lse, q, k_nope, v, k_rope, cache_lengths, valid_length,
+                                 cache_row_offsets, cache_offsets, scale, lse=None, k_rope_scale=None, q_scale=None,
+                                 k_nope_scale=None, v_scale=None, q_max_seq_len=0, stream=None, mask="causal"):
+    """mla_prefill_ragged_row with K_rope given as this row's rows laid out like K: k_rope
+    [rows, 1, 64] of q's element type (float8_e4m3fn with k_rope_scale [1] float32)."""
+    T, H, qd = q.shape
+    _contiguous(output=output, lse=lse, acc=acc, acc_lse=acc_lse, q=q, k_nope=k_nope, v=v, k_rope=k_rope)
+    _shapes(T, H, rows=[("output", output), ("acc", acc)], lses=[("lse", lse), ("acc_lse", acc_lse)])
+    _kv(H, q.dtype, k_nope, v)
+    if k_rope.dim() != 3 or tuple(k_rope.shape[1:]) != (1, 64) or _dtype_code(k_rope) != _dtype_code(q):
+        raise ValueError(f"k_rope must be [rows, 1, 64] of q's element type, got {tuple(k_rope.shape)} {k_rope.dtype}")
+    _check(_lib.mla_prefill_ragged_row_krope(_ptr(output), _dtype_code(output), _f32(lse, "lse"), _f32(acc, "acc"),
+                                             _f32(acc_lse, "acc_lse"), _ptr(q), _dtype_code(q), _ptr(k_nope),
+                                             _ptr(v), _ptr(k_rope), _f32(k_rope_scale, "k_rope_scale"),
+                                             _idx(cache_lengths, "cache_lengths"), _idx(valid_length, "valid_length"),
+                                             _idx(cache_row_offsets, "cache_row_offsets"),
+                                             _idx(cache_offsets, "cache_offsets"), valid_length.shape[0] - 1, T, H,
+                                             qd, k_nope.shape[2], _mask_code(mask), float(scale), _ptr(q_scale),
+                                             _ptr(k_nope_scale), _ptr(v_scale), int(q_max_seq_len), _stream(stream)),
+           "mla_prefill_ragged_row_krope")
 
 
 def mla_prefill_latent_up(kv: PagedCache, layer_idx, buffer_row_offsets_r, cache_offsets_r, w_kv, k_nope, v,

@@ -458,6 +458,29 @@ mla_status_t mla_prefill_ragged_row(void* output, mla_dtype_t output_dtype, floa
                       num_heads, q_depth, depth, mask, scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream);
 }
 
+mla_status_t mla_prefill_ragged_row_krope(void* output, mla_dtype_t output_dtype, float* lse, float* acc,
+                                          float* acc_lse, const void* q, mla_dtype_t qkv_dtype, const void* k_nope,
+                                          const void* v, const void* k_rope, const float* k_rope_scale,
+                                          const uint32_t* cache_lengths, const uint32_t* valid_length,
+                                          const uint32_t* cache_row_offsets, const uint32_t* cache_offsets,
+                                          uint32_t batch_size, uint32_t total_q_tokens, uint32_t num_heads,
+                                          uint32_t q_depth, uint32_t depth, mla_mask_t mask, float scale,
+                                          const float* q_scale, const float* k_nope_scale, const float* v_scale,
+                                          uint32_t q_max_seq_len, void* stream) {
+  if (!k_rope || !cache_lengths) return MLA_ERR_NULL_ARG;
+  // the rows' element type is the query's; the descriptor carries only the start
+  // positions and the rows' scale
+  mla_paged_cache_t rows{};
+  rows.dtype = qkv_dtype;
+  rows.cache_lengths = cache_lengths;
+  rows.scale = k_rope_scale;
+  if (qkv_dtype != MLA_FP8_E4M3FN && k_rope_scale) return MLA_ERR_UNSUPPORTED_DTYPE;
+  return prefill_impl(output, output_dtype, lse, nullptr, nullptr, acc, acc_lse, true,
+                      QuerySource{q, nullptr, k_rope, false}, qkv_dtype, k_nope, v, &rows, 0, valid_length,
+                      cache_row_offsets, cache_offsets, batch_size, total_q_tokens, num_heads, q_depth, depth, mask,
+                      scale, q_scale, k_nope_scale, v_scale, q_max_seq_len, stream);
+}
+
 mla_status_t mla_prefill_ragged(void* output, mla_dtype_t output_dtype, const void* q, mla_dtype_t qkv_dtype,
                                 const void* k_nope, const void* v, const mla_paged_cache_t* k_rope,
                                 uint32_t layer_idx, const uint32_t* valid_length, const uint32_t* cache_row_offsets,

@@ -63,7 +63,7 @@ class PrefillStep:
     ``cap`` is the buffer-row capacity handed to the plan (default: the whole
     batch's context, one row).  ``gather_cols`` = (col_begin, col_count) of the
     cache rows the gather copies (default: the 64-column K_rope window, which the
-    attention of a one-row plan then reads; any other window is gathered only).  With ``kv_b_weight``
+    attention of each buffer row then reads; any other window is gathered only).  With ``kv_b_weight``
     ([H*256, latent_dim] bf16) K_nope / V are not the workload's tensors but are
     decompressed per buffer row from the latent cache (columns
     ``latent_col`` .. +latent_dim), which replaces the gather step.
@@ -179,13 +179,24 @@ class PrefillStep:
                              self.buffer_row_offsets[row], co, self.w.softmax_scale, sc.get("q"),
                              sc.get("k_nope"), sc.get("v"), self.w.max_q, stream, mask=self.mask)
 
-    def attention_row_merged(self, row: int, stream=None):
+    def attention_row_merged(self, row: int, stream=None, rope="gathered"):
         """Attention over plan row ``row`` of several (rows run in order): each
         token's partial is carried in the fp32 accumulator from its sequence's
         first row to the row holding its last visible key, which writes the bf16
-        output."""
+        output.  K_rope comes from the row's gathered rows (the gather of this
+        row must have run) when the step gathers them (``rope="gathered"``), else
+        (or with ``rope="paged"``) through the page table."""
         kn, v = self.row_buffers(row)
         sc = self.scales or {}
+        if rope == "gathered" and self.rope_gather:
+            B.mla_prefill_ragged_row_krope(self.out, self.acc, self.lse, self.q, kn, v,
+                                           self.gathered.view(self.cap, 1, 64), self.cache_lengths,
+                                           self.input_row_offsets, self.buffer_row_offsets[row],
+                                           self.cache_offsets[row], self.w.softmax_scale,
+                                           k_rope_scale=sc.get("k_rope"), q_scale=sc.get("q"),
+                                           k_nope_scale=sc.get("k_nope"), v_scale=sc.get("v"),
+                                           q_max_seq_len=self.w.max_q, stream=stream, mask=self.mask)
+            return
         B.mla_prefill_ragged_row(self.out, self.acc, self.lse, self.q, kn, v, self.kv, self.w.spec.layer_idx,
                                  self.input_row_offsets, self.buffer_row_offsets[row], self.cache_offsets[row],
                                  self.w.softmax_scale, q_scale=sc.get("q"), k_nope_scale=sc.get("k_nope"),

@@ -1,5 +1,6 @@
-"""Attention with K_rope given as rows laid out like K (mla_prefill_ragged_krope)
-on the GPU against the float64 oracle.
+"""Attention with K_rope given as rows laid out like K (mla_prefill_ragged_krope, and
+mla_prefill_ragged_row_krope for the rows of a multi-row plan) on the GPU against the
+float64 oracle.
 
 Bars: max |gpu - oracle| <= 1e-2 (bf16; on tokens that see 1..5 keys the error
 beyond half a bf16 ulp of the output, <= 5e-3, as in the other bf16 tests) and
@@ -173,3 +174,40 @@ def test_step_gather_feeds_the_attention():
     step.attention(0, out=paged, rope="paged")
     torch.cuda.synchronize()
     assert torch.equal(paged, step.out)
+
+
+@pytest.mark.parametrize("mask", ["causal", "null"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_rows_read_their_gathered_window(dtype, mask):
+    """A plan of several buffer rows: each row's attention reads that row's gathered K_rope
+    window (mla_prefill_ragged_row_krope).  The output equals the same rows read through the
+    page table bit for bit (the same arithmetic on the same values) and the oracle over every
+    key (one row holding all of them)."""
+    kw = CASES[0]
+    say(f"rows gathered {kw} {dtype} {mask}")
+    w = _workload(kw, dtype, 970)
+    step = PrefillStep(w, "cuda", cap=150, mask=mask)
+    assert step.rows >= 2
+    step.out.fill_(float("nan"))
+    step.acc.fill_(float("nan"))
+    step.lse.fill_(float("nan"))
+    step.run()
+    torch.cuda.synchronize()
+    check_plan(step, w)
+    gathered = step.out.clone()
+    step.out.fill_(float("nan"))
+    step.acc.fill_(float("nan"))
+    for r in range(step.rows):
+        step.attention_row_merged(r, rope="paged")
+    torch.cuda.synchronize()
+    assert torch.equal(gathered, step.out)
+    bro1, co1, _, st = oracle.plan(w.input_row_offsets, w.cache_lengths, max(1, w.total_ctx), 1)
+    assert st == 0
+    ref = oracle.mla_prefill_ragged(w.q, w.k_nope, w.v, w.cache, 0, w.page_table, w.spec.page_size, w.spec.rope_col,
+                                    w.cache_lengths, w.input_row_offsets, bro1[0], co1[0], w.softmax_scale,
+                                    scales=w.scales, mask=mask)
+    if dtype == "bf16":
+        report_keys(gathered.float().cpu().numpy(), ref, visible_keys(w, bro1[0], co1[0], mask), BAR[dtype],
+                    "rows gathered")
+    else:
+        assert report(gathered.float().cpu().numpy(), ref, BAR[dtype], "rows gathered fp8") <= BAR[dtype]

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
                                     "mla_prefill_last_hip_error", "mla_prefill_latent_up", "mla_prefill_merge",
                                     "mla_prefill_plan", "mla_prefill_ragged", "mla_prefill_ragged_krope",
                                     "mla_prefill_ragged_kvsplit", "mla_prefill_ragged_kvsplit_noalloc",
-                                    "mla_prefill_ragged_lse", "mla_prefill_ragged_row", "mla_prefill_ragged_split",
+                                    "mla_prefill_ragged_lse", "mla_prefill_ragged_row", "mla_prefill_ragged_row_krope",
+                                    "mla_prefill_ragged_split",
                                     "mla_prefill_set_debug", "mla_status_string"]
 
 
@@ -324,6 +325,28 @@ def test_krope_validation_without_gpu():
     assert lib.mla_prefill_ragged_krope(*args(rows=ctypes.c_void_p(264))) == 2   # rows not 16-byte aligned
     assert lib.mla_prefill_ragged_krope(*args(out=None)) == 1
     assert lib.mla_prefill_ragged_krope(*args(b=0)) == 0                      # empty batch: a no-op
+
+
+def test_row_krope_validation_without_gpu():
+    """mla_prefill_ragged_row_krope: the row call's and the contiguous rows' host-side checks
+    return their codes before anything is enqueued."""
+    import mla_ragged_paged_amd._binding as b
+    lib = b._lib
+    d = ctypes.c_void_p(256)
+
+    def args(**kw):
+        return [kw.get("out", d), 0, None, kw.get("acc", d), kw.get("acc_lse", d), d, kw.get("qdt", 0), d, d,
+                kw.get("rows", d), kw.get("rs"), kw.get("cl", d), d, d, None, kw.get("b", 1), 4, 2, 192, 128,
+                kw.get("mask", 0), ctypes.c_float(0.07), kw.get("qs"), kw.get("qs"), kw.get("qs"), 0, None]
+    assert lib.mla_prefill_ragged_row_krope(*args(acc=None)) == 1            # row mode needs the accumulator
+    assert lib.mla_prefill_ragged_row_krope(*args(acc_lse=None)) == 1
+    assert lib.mla_prefill_ragged_row_krope(*args(rows=None)) == 1           # no K_rope rows
+    assert lib.mla_prefill_ragged_row_krope(*args(cl=None)) == 1             # no start positions
+    assert lib.mla_prefill_ragged_row_krope(*args(rs=d)) == 3                # a rows scale for bf16
+    assert lib.mla_prefill_ragged_row_krope(*args(qdt=1, qs=d)) == 1         # e4m3 rows without their scale
+    assert lib.mla_prefill_ragged_row_krope(*args(mask=3)) == 5
+    assert lib.mla_prefill_ragged_row_krope(*args(acc=ctypes.c_void_p(264))) == 2   # acc not 16-byte aligned
+    assert lib.mla_prefill_ragged_row_krope(*args(b=0)) == 0                 # empty batch: a no-op
 
 
 def test_kvsplit_noalloc_validation_without_gpu():
