@@ -66,7 +66,8 @@ class PrefillStep:
     attention of each buffer row then reads; any other window is gathered only).  With ``kv_b_weight``
     ([H*256, latent_dim] bf16) K_nope / V are not the workload's tensors but are
     decompressed per buffer row from the latent cache (columns
-    ``latent_col`` .. +latent_dim), which replaces the gather step.
+    ``latent_col`` .. +latent_dim); the gather then lays out only the K_rope
+    window.
     ``split_keys`` > 0 (one buffer row only) runs the attention through
     mla_prefill_ragged_kvsplit with that threshold and a workspace allocated
     here; "auto" takes balanced_split_keys of the workload.
@@ -100,7 +101,7 @@ class PrefillStep:
         self.cache_offsets = torch.zeros((self.rows, Bsz), dtype=torch.int32, device=dev)
         self.buffer_lengths = torch.zeros((self.rows,), dtype=torch.int32, device=dev)
         self.status = torch.zeros((1,), dtype=torch.int32, device=dev)
-        self.rope_gather = gather_cols is None and kv_b_weight is None
+        self.rope_gather = gather_cols is None
         self.gather_cols = (w.spec.rope_col, 64) if gather_cols is None else tuple(gather_cols)
         self.gathered = torch.zeros((self.cap, self.gather_cols[1]), dtype=w.cache.dtype, device=dev)
         self.out = torch.zeros((w.total_q, w.heads, 128), dtype=torch.bfloat16, device=dev)
@@ -203,14 +204,15 @@ class PrefillStep:
                                  v_scale=sc.get("v"), q_max_seq_len=self.w.max_q, stream=stream, mask=self.mask)
 
     def run(self, stream=None):
-        """The whole step: plan, then per buffer row its gather (or its latent
-        decompression) and its attention (merged across rows when there are several)."""
+        """The whole step: plan, then per buffer row its gather (with a weight
+        matrix, its latent decompression and the gather of the K_rope window) and
+        its attention (merged across rows when there are several)."""
         self.plan(stream)
         latent = self.kv_b_weight is not None
         for r in range(self.rows):
             if latent:
                 self.latent_up(r, stream)
-            else:
+            if not latent or self.rope_gather:
                 self.gather(r, stream)
             if self.rows == 1:
                 kn, v = self.row_buffers(0)
