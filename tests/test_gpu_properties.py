@@ -8,7 +8,10 @@ drawn case, through the C-ABI:
 * plan outputs and every plan row's gather equal the oracle bit for bit;
 * with one buffer row, the attention (causal, and null mask for half the
   cases) equals the oracle on every output within the bars of the flat tests
-  (max |gpu - oracle| <= 1e-2 bf16, <= 6e-2 fp8 with bf16 output).
+  (max |gpu - oracle| <= 1e-2 bf16, <= 6e-2 fp8 with bf16 output);
+* when the drawn capacity cuts the contexts into several rows, the whole step
+  over those rows (each row's gathered K_rope window read by its attention,
+  partials carried per token) meets the same bars against the same oracle.
 
 Bounded: a fixed number of examples, derandomised, no deadline, no shrinking
 (the first failing example is reported as drawn), no example database.
@@ -92,3 +95,19 @@ def test_random_batches_plan_gather_attention(c):
     # output itself (half an ulp reaches 1.6e-2 for |o| in [4, 8)), as in the flat tests
     half_ulp = 0.5 * np.ldexp(1.0, np.frexp(np.abs(ref[few]))[1] - 8)
     assert float((err[few] - half_ulp).max(initial=0.0)) <= (bar if c["dtype"] == "fp8" else 5e-3)
+    # the same attention through the rows of the capacity-C/cap_div plan: each row
+    # gathers its K_rope window and its attention reads it, each token finishing in
+    # the row that holds its last visible key; no accumulator value is preset
+    if step.rows > 1:
+        rows = PrefillStep(w, "cuda", cap=cap, mask=c["mask"])
+        rows.out.fill_(float("nan"))
+        rows.acc.fill_(float("nan"))
+        rows.lse.fill_(float("nan"))
+        rows.run()
+        torch.cuda.synchronize()
+        got_r = rows.out.float().cpu().numpy()
+        err_r = np.abs(got_r - ref)
+        say(f"  {rows.rows} rows: max|gpu - oracle| = {float(err_r.max()):.3e}")
+        assert not np.isnan(got_r).any()
+        assert float(err_r[~few].max(initial=0.0)) <= bar
+        assert float((err_r[few] - half_ulp).max(initial=0.0)) <= (bar if c["dtype"] == "fp8" else 5e-3)
