@@ -14,7 +14,7 @@ namespace mla {
 // most MLA_MAX_BATCH) and then writes the plan rows assigned to it.
 __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   extern __shared__ uint64_t S[];             // [B + 1] context prefix sums
-  __shared__ uint64_t part[256];
+  __shared__ uint64_t part[4];                // per-wave totals
   const uint32_t tid = threadIdx.x;
   const uint32_t B = a.batch;
   const uint32_t per = (B + 255u) / 256u;
@@ -25,15 +25,21 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
     S[b + 1] = L;
     sum += L;
   }
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t acc = 0;
-    for (int i = 0; i < 256; ++i) { const uint64_t t = part[i]; part[i] = acc; acc += t; }
-    S[0] = 0;
+  // exclusive prefix of the 256 threads' sums: inclusive scan within each wave
+  // (64-bit values moved as two 32-bit shuffles), then the waves' totals
+  const int lane = (int)(tid & 63u), wv = (int)(tid >> 6);
+  uint64_t incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)incl, (unsigned)d, 64);
+    const uint32_t hi = __shfl_up((uint32_t)(incl >> 32), (unsigned)d, 64);
+    if (lane >= d) incl += ((uint64_t)hi << 32) | lo;
   }
+  if (lane == 63) part[wv] = incl;
+  if (tid == 0) S[0] = 0;
   __syncthreads();
-  uint64_t acc = part[tid];
+  uint64_t acc = incl - sum;
+  for (int i = 0; i < wv; ++i) acc += part[i];
   for (uint32_t b = b0; b < b1; ++b) { acc += S[b + 1]; S[b + 1] = acc; }
   __syncthreads();
 
