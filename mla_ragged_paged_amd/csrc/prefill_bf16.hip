@@ -237,11 +237,16 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int m = 2 * wu + u;
-      const int32_t j = min(kt * BN + kr_row[u], jend - 1);
-      const uint32_t pos = (uint32_t)(c0 + j);
-      const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
-      const uint32_t off = contig ? (uint32_t)(j - kt * BN) * 128u + 16u * kr_chunk[u]
-                                  : (pg[u] * a.page_size + slot) * cache_row + a.rope_col * 2 + 16u * kr_chunk[u];
+      uint32_t off;
+      if (contig) {
+        // the tile's descriptor ends at the last key: rows past it read as zeros
+        off = (uint32_t)kr_row[u] * 128u + 16u * kr_chunk[u];
+      } else {
+        const int32_t j = min(kt * BN + kr_row[u], jend - 1);
+        const uint32_t pos = (uint32_t)(c0 + j);
+        const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
+        off = (pg[u] * a.page_size + slot) * cache_row + a.rope_col * 2 + 16u * kr_chunk[u];
+      }
       bload_lds(kr_t, off, st + KR_OFF + m * 1024);
     }
   };
@@ -430,7 +435,15 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         tile_body(std::false_type{});
     }
     };
-    step((MLA_LDS uint8_t*)lds + (stage ^ 1) * STAGE, (const MLA_LDS uint8_t*)lds + stage * STAGE);
+    // the stage is a constant in each copy of the tile code, so the LDS read
+    // addresses take it as an immediate offset
+    // (the key-split forms keep one copy: two exceed the register budget there)
+    if constexpr (KVSPLIT)
+      step((MLA_LDS uint8_t*)lds + (stage ^ 1) * STAGE, (const MLA_LDS uint8_t*)lds + stage * STAGE);
+    else if (stage)
+      step((MLA_LDS uint8_t*)lds, (const MLA_LDS uint8_t*)lds + STAGE);
+    else
+      step((MLA_LDS uint8_t*)lds + STAGE, (const MLA_LDS uint8_t*)lds);
   }
 
   // ---- epilogue: combine the two halves' row sums, normalise, store the row
