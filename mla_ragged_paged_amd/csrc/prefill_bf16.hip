@@ -23,9 +23,11 @@
 //        row max / sum need one exchange between the wave's two 32-lane halves;
 //   online softmax in the exp2 domain: p = exp2(s*c - m*c), c = |scale|*log2(e)
 //        (a negative scale is applied by flipping the sign of Q, which is
-//        exact).  The running max m only moves when some row's tile max
-//        exceeds it by more than RESCALE_LOG2 (in log2 units), so the O
-//        rescale is skipped on most tiles; p then stays below 2^RESCALE_LOG2.
+//        exact).  The reference m is set to the row max on the first tile
+//        and moves only when the weights some lane computes for a tile sum
+//        to more than 2^16 (or are not finite): then m becomes the running
+//        max, O and the row sum are rescaled and the tile's weights are
+//        computed again.  Most tiles take neither the max nor the rescale.
 //        p is rounded to bf16 once and the row sum is taken over the rounded
 //        values (v_dot2 against (1, 1)), so the weights applied to V are
 //        normalised exactly.  Masks are applied only on tiles that straddle
@@ -49,7 +51,7 @@ constexpr int BM = 128;            // queries per workgroup
 constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
 constexpr int DQK = 192, DNOPE = 128, DV = 128;
-constexpr float RESCALE_LOG2 = 8.0f;
+constexpr float WSUM_MAX = 65536.0f;   // 2^WSUM_LOG2, WSUM_LOG2 = 16: bound on a lane's weight sum per tile
 
 // LDS stage layout (bytes)
 constexpr int KN_OFF = 0;                      // K_nope [64 rows][16 chunks of 16 B]
@@ -271,10 +273,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 
   // ---- running softmax state (raw score units) and output accumulator O^T
   const float c = a.scale_log2;                      // |scale| * log2(e), > 0
-  const float thr = RESCALE_LOG2 / c;                // rescale threshold in raw units
   float m_run = -1e30f;                              // finite, so (m_old - m_new) stays defined
   float mc = m_run * c;
   float l_run = 0.f;                                 // this lane's share of the row sum
+  bool fresh = true;                                 // no tile computed yet (wave-uniform)
   f32x16 o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = f32x16{};
@@ -380,29 +382,21 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
         }
       };
       vread(0, vf[0]);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = max_across_halves(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        m_run = m_new;
-        mc = m_run * c;
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] *= alpha;
-      }
+      asm volatile("" ::: "memory");   // keeps these reads ahead of the branches below
+      // Weights p = exp2(s c - m c) against the running reference m.  The tile's
+      // row max is taken only on the unit's first tile and when some lane's
+      // weights leave the range the reference keeps them in (their sum above
+      // 2^WSUM_LOG2, or not finite); then m moves to the max, O and l are
+      // rescaled, and the weights are computed again (each is then at most 1).
       uint32_t pw[16];
+      float ps = 0.f;
+      auto weights = [&]() {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          pw[8 * kb + x] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * x], c, -mc)),
-                                       __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * x + 1], c, -mc)));
-      {
+          for (int x = 0; x < 8; ++x)
+            pw[8 * kb + x] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * x], c, -mc)),
+                                         __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * x + 1], c, -mc)));
         typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         float ps0 = 0.f, ps1 = 0.f;
@@ -411,8 +405,31 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
           ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x]), ones, ps0, false);
           ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x + 1]), ones, ps1, false);
         }
-        l_run += ps0 + ps1;
+        ps = ps0 + ps1;
+      };
+      bool redo = fresh;
+      fresh = false;
+      if (!redo) {
+        weights();
+        redo = __builtin_amdgcn_ballot_w64(!(ps <= WSUM_MAX)) != 0;
       }
+      if (redo) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = max_across_halves(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        mc = m_run * c;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] *= alpha;
+        weights();
+      }
+      l_run += ps;
 
       // O^T += V^T P^T, four (two) 16-key steps; V fragments are read one step ahead
       __builtin_amdgcn_s_setprio(1);

@@ -62,6 +62,53 @@ def test_small_ragged_every_output(case):
     assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, f"small{case}") <= BAR_BF16
 
 
+
+def _log2_scores(w, b, h):
+    """Scores of sequence b, head h in log2 units (scale * q.k * log2 e), [n_b, p_b + n_b]
+    (keys of the sequence in cache order), from the bf16 inputs widened exactly."""
+    t0, n = int(w.input_row_offsets[b]), int(w.n[b])
+    g0 = int((w.n[:b] + w.p[:b]).sum())
+    ctx = int(w.p[b]) + n
+    q = w.q[t0:t0 + n, h].double().cpu().numpy()
+    kn = w.k_nope[g0:g0 + ctx, h].double().cpu().numpy()
+    kr = oracle.rope_rows(w.cache, w.spec.layer_idx, w.page_table, w.spec.page_size, w.spec.rope_col, b,
+                          range(ctx))
+    return w.softmax_scale * (q @ np.concatenate([kn, kr], axis=1).T) * np.log2(np.e)
+
+
+@pytest.mark.parametrize("scale", [2.0, -2.0])
+def test_running_reference_moves_after_the_first_tile(scale):
+    """With a large softmax scale, some rows' scores on a later 64-key tile exceed the
+    maximum over all their earlier tiles by more than 16 in log2 units.  Against the
+    running reference (never above that maximum) such a tile's weights then sum to more
+    than 2^16 for the lane holding the key, so the kernel takes the tile's max, rescales
+    and computes the weights again.  The case first shows on the oracle's scores that
+    such tiles occur, then compares every output.  At this scale most outputs are
+    averages of a few value rows, so V is halved (exact in bf16): outputs then stay
+    below 4 in magnitude, where the bf16 rounding of the output alone keeps within the
+    bar (as for tokens that see only a few keys)."""
+    spec = workloads.Spec("remax", 2, (0, 0), (0, 0), 2, 128, True, "bf16", row_width=576, rope_col=512,
+                          seed=197)
+    w = workloads.build(spec, n=[160, 40], p=[700, 90])
+    w.softmax_scale = scale
+    w.v.mul_(0.5)
+    x = _log2_scores(w, 0, 0)
+    p0 = int(w.p[0])
+    jumps = 0
+    for i in range(x.shape[0]):
+        vis = p0 + i + 1
+        run = x[i, :min(64, vis)].max()
+        for kt in range(1, (vis + 63) // 64):
+            mx = x[i, kt * 64:min((kt + 1) * 64, vis)].max()
+            jumps += int(mx > run + 16.0)
+            run = max(run, mx)
+    say(f"bf16 scale {scale}: {jumps} tiles whose max exceeds every earlier tile's by more than 16 (log2)")
+    assert jumps > 0
+    step = _run(w)
+    bro, co, _ = check_plan(step, w)
+    ref = oracle_full(w, bro[0], co[0])
+    assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, f"remax{scale}") <= BAR_BF16
+
 def _row_buffers(w, bro_r, co_r):
     """K_nope / V of one plan row, laid out as a gather of K/V entries would leave them."""
     L = w.n + w.p
