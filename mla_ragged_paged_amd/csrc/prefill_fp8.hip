@@ -255,12 +255,17 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
                              : cr_rs;
 #pragma unroll
     for (int u = 0; u < KRL; ++u) {
-      const int32_t j = min(kt * BN + kr_row[u], jend - 1);
-      const uint32_t pos = (uint32_t)(c0 + j);
-      const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
-      const uint32_t el = QM == 2 ? 2u : 1u;
-      const uint32_t off = contig ? (uint32_t)(j - kt * BN) * (uint32_t)KR_ROW + 16u * kr_chunk[u]
-                                  : (pg[u] * a.page_size + slot) * cache_row + a.rope_col * el + 16u * kr_chunk[u];
+      uint32_t off;
+      if (contig) {
+        // the tile's descriptor ends at the last key: rows past it read as zeros
+        off = (uint32_t)kr_row[u] * (uint32_t)KR_ROW + 16u * kr_chunk[u];
+      } else {
+        const int32_t j = min(kt * BN + kr_row[u], jend - 1);
+        const uint32_t pos = (uint32_t)(c0 + j);
+        const uint32_t slot = a.page_shift < 32u ? (pos & (a.page_size - 1u)) : (pos % a.page_size);
+        const uint32_t el = QM == 2 ? 2u : 1u;
+        off = (pg[u] * a.page_size + slot) * cache_row + a.rope_col * el + 16u * kr_chunk[u];
+      }
       bload_lds(kr_t, off, st + KR_OFF + (KRL * wu + u) * 1024);
     }
   };
@@ -315,7 +320,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   constexpr bool MFMA_ROWSUM = CAUSAL;
   f32x16 lsum = f32x16{};
   const int one4 = 0x38383838;                       // four e4m3 1.0
-  const i32x8 ones8 = {one4, one4, one4, one4, one4, one4, one4, one4};
+  i32x8 ones8 = {one4, one4, one4, one4, one4, one4, one4, one4};
 
   // ---- prologue, ordered for the first tile's critical path: page ids first,
   // then the K_nope / V rows, then Q, so the K_rope loads wait for the page ids only
@@ -342,6 +347,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   auto step = [&](int32_t kt, const uint8_t* st, uint8_t* next) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // the all-ones operand stays in its registers across tiles instead of being
+    // rebuilt with eight moves in each
+    if constexpr (MFMA_ROWSUM) asm volatile("" : "+v"(ones8));
     if (kt == kt_lo && a.scale < 0.f) {
 #pragma unroll
       for (int ks = 0; ks < QKS; ++ks) qop[ks] ^= (int)0x80808080;
@@ -443,7 +451,9 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int kb = x >> 2, r = 4 * (x & 3);
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r], e[kb][r + 1], 0, false);
+        // the first conversion's untouched half is overwritten by the second, so
+        // its "old" operand is any dead register (no copy of a zero needed)
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r], e[kb][r + 1], __builtin_bit_cast(int, e[kb][r]), false);
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r + 2], e[kb][r + 3], wd, true);
         pq[x] = wd;
       }
