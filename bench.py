@@ -232,7 +232,7 @@ def _alternating_median_ms(torch, fns, reps, stream):
     return out
 
 
-def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
+def next_rows_bench(torch, w, reps=9):
     """The paths beside the headline step, on the same workload:
     the null mask (every key visible), the context cut into three buffer rows
     whose partials merge in the attention epilogue, the split-query calls (also
@@ -266,12 +266,19 @@ def next_rows_bench(torch, w, one_row_attention_ms, reps=9):
         for r in range(mr.rows):
             mr.attention_row_merged(r)
     attn_med, attn_best = _median_ms(torch, rows_attention, reps, stream)
+    # the ratio to one row is taken against one-row launches timed in alternation
+    # with the rows (the same clock state; the headline is timed minutes earlier)
+    one = PrefillStep(w, "cuda:0")
+    one.run()
+    alt_rows, alt_one = _alternating_median_ms(torch, [rows_attention, lambda: one.attention(0)], reps, stream)
+    del one
     fl = workloads.causal_flops(w.n, w.p, w.heads)
     out["rows_merged"] = {"cap": cap, "rows": mr.rows, "step_median_ms": round(step_med, 4),
                           "attention_median_ms": round(attn_med, 4), "attention_min_ms": round(attn_best, 4),
                           "achieved_TFLOPs": round(fl / (attn_med * 1e-3) / 1e12, 2),
                           "frac_of_peak": round(fl / (attn_med * 1e-3) / 1e12 / peak, 4),
-                          "attention_time_vs_one_row": round(attn_med / one_row_attention_ms, 3)}
+                          "attention_time_vs_one_row": round(alt_rows / alt_one, 3),
+                          "alternating_ms": {"rows": round(alt_rows, 4), "one_row": round(alt_one, 4)}}
     del mr
 
     # split query: bf16 on this workload (contiguous K_rope rows), and the fp8
@@ -511,7 +518,7 @@ def main():
         print("[bench] gather bandwidth on a >= 1 GiB paged cache", file=sys.stderr, flush=True)
         guarded("gather_bench", lambda: gather_bench(torch))
         print("[bench] null mask, buffer rows, split query, decompression, graphs, merge", file=sys.stderr, flush=True)
-        guarded("next_rows", lambda: next_rows_bench(torch, w, attn_median))
+        guarded("next_rows", lambda: next_rows_bench(torch, w))
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         guarded("cpu_baseline", lambda: cpu_baseline(w, args.cpu_seconds))
