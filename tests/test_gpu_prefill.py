@@ -76,8 +76,9 @@ def _log2_scores(w, b, h):
     return w.softmax_scale * (q @ np.concatenate([kn, kr], axis=1).T) * np.log2(np.e)
 
 
+@pytest.mark.parametrize("mask", ["causal", "null"])
 @pytest.mark.parametrize("scale", [2.0, -2.0])
-def test_running_reference_moves_after_the_first_tile(scale):
+def test_running_reference_moves_after_the_first_tile(scale, mask):
     """With a large softmax scale, some rows' scores on a later 64-key tile exceed the
     maximum over all their earlier tiles by more than 16 in log2 units.  Against the
     running reference (never above that maximum) such a tile's weights then sum to more
@@ -96,18 +97,39 @@ def test_running_reference_moves_after_the_first_tile(scale):
     p0 = int(w.p[0])
     jumps = 0
     for i in range(x.shape[0]):
-        vis = p0 + i + 1
+        vis = p0 + i + 1 if mask == "causal" else x.shape[1]
         run = x[i, :min(64, vis)].max()
         for kt in range(1, (vis + 63) // 64):
             mx = x[i, kt * 64:min((kt + 1) * 64, vis)].max()
             jumps += int(mx > run + 16.0)
             run = max(run, mx)
-    say(f"bf16 scale {scale}: {jumps} tiles whose max exceeds every earlier tile's by more than 16 (log2)")
+    say(f"bf16 scale {scale} {mask}: {jumps} tiles whose max exceeds every earlier tile's by more than 16 (log2)")
     assert jumps > 0
-    step = _run(w)
+    step = PrefillStep(w, "cuda", mask=mask)
+    step.run()
+    torch.cuda.synchronize()
     bro, co, _ = check_plan(step, w)
-    ref = oracle_full(w, bro[0], co[0])
-    assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, f"remax{scale}") <= BAR_BF16
+    ref = oracle_full(w, bro[0], co[0], mask=mask)
+    assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, f"remax{scale}{mask}") <= BAR_BF16
+
+
+@pytest.mark.parametrize("mask", ["causal", "null"])
+def test_running_reference_moves_in_buffer_rows(mask):
+    """The same inputs (scale 2) with the context cut into four buffer rows: each row's
+    launch restarts the reference on its first tile and carries the partial rows
+    between launches; the merged output is compared with the oracle over all keys."""
+    spec = workloads.Spec("remax", 2, (0, 0), (0, 0), 2, 128, True, "bf16", row_width=576, rope_col=512,
+                          seed=197)
+    w = workloads.build(spec, n=[160, 40], p=[700, 90])
+    w.softmax_scale = 2.0
+    w.v.mul_(0.5)
+    step = PrefillStep(w, "cuda", cap=300, mask=mask)
+    step.run()
+    torch.cuda.synchronize()
+    assert step.rows >= 4
+    full = np.concatenate([[0], np.cumsum(w.n + w.p)]).astype(np.uint32)
+    ref = oracle_full(w, full, np.zeros(w.batch, dtype=np.uint32), mask=mask)
+    assert report(step.out.float().cpu().numpy(), ref, BAR_BF16, f"remax-rows-{mask}") <= BAR_BF16
 
 def _row_buffers(w, bro_r, co_r):
     """K_nope / V of one plan row, laid out as a gather of K/V entries would leave them."""
