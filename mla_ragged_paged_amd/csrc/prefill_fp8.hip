@@ -5,9 +5,13 @@
 // float8_e4m3fn and the output is then bfloat16; the k_rope_scales overload);
 // every fp8 operand stands for code * scale of its tensor.
 //
-// Same work decomposition, LDS staging and online softmax as the bf16 kernel
-// (BM = 128 queries per workgroup of four waves, BN = 64 keys per tile, two
-// direct-to-LDS stages, S^T with one query per lane column); what differs:
+// Same work decomposition and LDS staging as the bf16 kernel (BM = 128 queries
+// per workgroup of four waves, BN = 64 keys per tile, two direct-to-LDS stages,
+// S^T with one query per lane column) and an online softmax in the exp2 domain;
+// what differs:
+//   * the running max moves when a row's tile max exceeds it by more than
+//     RESCALE_LOG2, so every weight stays at most 2^RESCALE_LOG2 (below the
+//     e4m3 maximum of 448) on every tile;
 //   * S^T = K . Q^T runs on the fp8 32x32x64 MFMA: two k-steps over the 128
 //     nope columns, then one over the 64 rope columns.  The nope partial sum is
 //     multiplied by s_knope / s_krope before the rope step, and
