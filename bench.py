@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -40,14 +41,23 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}      # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks and empty lines (the kernel sources
+    hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(dtype: str = "bf16") -> str:
-    """Hash of the attention kernel sources of one dtype (its .hip file and the shared headers):
-    a committed traffic summary is used only when it was taken on these sources."""
+    """Hash of the code of the attention kernel sources of one dtype (its .hip file and the
+    shared headers, comments left out): a committed traffic summary is used only when it
+    was taken on this code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mla_ragged_paged_amd", "csrc")
     for name in sorted([f"prefill_{dtype}.hip", "device_common.h", "kernels.h"]):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update((name + _code_only(f.read())).encode())
     return h.hexdigest()[:16]
 
 
