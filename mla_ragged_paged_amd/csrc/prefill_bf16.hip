@@ -51,7 +51,7 @@ constexpr int BM = 128;            // queries per workgroup
 constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
 constexpr int DQK = 192, DNOPE = 128, DV = 128;
-constexpr float WSUM_MAX = 65536.0f;   // 2^WSUM_LOG2, WSUM_LOG2 = 16: bound on a lane's weight sum per tile
+constexpr float WSUM_MAX = 65536.0f;   // 2^16: bound on one lane's weight sum over a tile
 
 // LDS stage layout (bytes)
 constexpr int KN_OFF = 0;                      // K_nope [64 rows][16 chunks of 16 B]
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       // Weights p = exp2(s c - m c) against the running reference m.  The tile's
       // row max is taken only on the unit's first tile and when some lane's
       // weights leave the range the reference keeps them in (their sum above
-      // 2^WSUM_LOG2, or not finite); then m moves to the max, O and l are
+      // WSUM_MAX, or not finite); then m moves to the max, O and l are
       // rescaled, and the weights are computed again (each is then at most 1).
       uint32_t pw[16];
       float ps = 0.f;
