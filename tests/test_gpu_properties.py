@@ -2,8 +2,10 @@
 
 Hypothesis draws the batch ("generic_flare_mla_prefill_ragged_paged_plan",
 Args): sequence count, new tokens n_b, cached prefixes p_b, page size,
-buffer-row capacity, head count H <= 8, and bf16 or fp8 inputs.  For each
-drawn case, through the C-ABI:
+buffer-row capacity, head count H <= 8, bf16 or fp8 inputs, and the softmax
+scale (1/sqrt(192) for half the cases, else 0.5, 2 or -2, which move the
+running max between key tiles; V is then halved exactly so outputs stay
+below 4 in magnitude).  For each drawn case, through the C-ABI:
 
 * plan outputs and every plan row's gather equal the oracle bit for bit;
 * with one buffer row, the attention (causal, and null mask for half the
@@ -44,7 +46,8 @@ def cases(draw):
     mask = draw(st.sampled_from(["causal", "null"]))
     cap_div = draw(st.integers(1, 3))
     seed = draw(st.integers(0, 10 ** 6))
-    return dict(n=n, p=p, heads=heads, ps=ps, dtype=dtype, mask=mask, cap_div=cap_div, seed=seed)
+    scale = draw(st.sampled_from([None, None, None, 0.5, 2.0, -2.0]))    # None: 1/sqrt(192)
+    return dict(n=n, p=p, heads=heads, ps=ps, dtype=dtype, mask=mask, cap_div=cap_div, seed=seed, scale=scale)
 
 
 def _bits(t):
@@ -59,6 +62,15 @@ def test_random_batches_plan_gather_attention(c):
     spec = workloads.Spec("prop", len(c["n"]), (0, 0), (0, 0), c["heads"], c["ps"], True, c["dtype"],
                           seed=c["seed"])
     w = workloads.build(spec, n=c["n"], p=c["p"])
+    if c["scale"] is not None:
+        # large scales move the running max between tiles; they also make outputs
+        # averages of a few value rows, so V is halved (exactly: the bf16 values, or
+        # the fp8 tensor's scale) to keep them below 4 in magnitude
+        w.softmax_scale = c["scale"]
+        if c["dtype"] == "fp8":
+            w.scales["v"] *= 0.5
+        else:
+            w.v.mul_(0.5)
     C = w.total_ctx
     cap = max(1, -(-C // c["cap_div"]))
     # plan and gather over every row of a plan with capacity C / cap_div
