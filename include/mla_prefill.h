@@ -261,7 +261,16 @@ mla_status_t mla_prefill_latent_up(const mla_paged_cache_t* kv, uint32_t layer_i
  *   cache_row_offsets device uint32 [batch_size+1], ragged K/V offsets.
  *   cache_offsets     device uint32 [batch_size] or NULL.
  *   q_depth, depth    must be 192 and 128 (DeepSeek V2/V3 geometry).
- *   scale             [host] softmax scale multiplying q.k.
+ *   scale             [host] softmax scale multiplying q.k; any sign, zero
+ *                     allowed.  The weights are formed in fp32 as
+ *                     exp2(s * c - m * c), c = |scale| * log2(e), m a running
+ *                     score: the rounding of m * c puts an absolute error of
+ *                     about 1e-7 * |scale * q.k| into each exponent, below the
+ *                     bf16 rounding of the weights while |scale * q.k| < 3e4.
+ *                     Larger products still give one-hot softmaxes exactly (the
+ *                     GPU tests go to |scale| = 1e4 on unit-variance inputs);
+ *                     |scale| above about 1e8 is outside the fp32 range of the
+ *                     formulation and not supported.
  *   q_scale, k_nope_scale, v_scale
  *                     fp8 only: device fp32 per-tensor dequantisation scales
  *                     (K_rope uses kv->scale); must be NULL for bf16.

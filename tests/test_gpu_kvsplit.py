@@ -218,3 +218,26 @@ def test_kvsplit_per_buffer_row_then_merged(dtype, mask):
             acc, acc_lse = merged, merged_lse
     torch.cuda.synchronize()
     assert report(acc.cpu().numpy(), ref, BAR[dtype], f"kvsplit-rows-{dtype}-{mask}") <= BAR[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_kvsplit_large_scale_with_rows_that_see_no_key_of_a_half(dtype):
+    """One 200-token sequence, split at 128 keys: its only tile is cut into keys 0..127
+    and 128..199, and queries 0..127 see none of the second half, which must hand the
+    merge an empty partial.  At a softmax scale of 1e4 (the top of the range the
+    header states) every softmax is one-hot: every output equals the oracle's, the
+    V row of the top key."""
+    spec = workloads.Spec("kvs-large", 1, (0, 0), (0, 0), 2, 16, True, dtype, row_width=576, rope_col=512, seed=733)
+    w = workloads.build(spec, n=[200], p=[0])
+    w.softmax_scale = 1e4
+    step = PrefillStep(w, "cuda")
+    step.run()
+    torch.cuda.synchronize()
+    bro = np.array([0, 200], dtype=np.uint32)
+    ref = oracle_full(w, bro, np.zeros(1, dtype=np.uint32))
+    got = torch.full_like(step.out, float("nan"))
+    _kvsplit(step, 128, out=got)
+    g = got.float().cpu().numpy()
+    assert not np.isnan(g).any()
+    assert report(g, ref, BAR[dtype], f"kvsplit-large-{dtype}") <= BAR[dtype]
+    assert report(step.out.float().cpu().numpy(), ref, BAR[dtype], f"plain-large-{dtype}") <= BAR[dtype]
