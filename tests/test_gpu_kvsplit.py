@@ -1,7 +1,7 @@
 """Key split (mla_prefill_ragged_kvsplit) on the GPU, against the float64 oracle
 and against the plain attention.
 
-Bars (spec tolerances for the output, written here): max |gpu - oracle|
+Bars (the accuracy bars of the output, written here): max |gpu - oracle|
 <= 1e-2 with bf16 inputs and <= 6e-2 with float8_e4m3fn inputs; log-sum-exp
 bars 1e-2 and 6.5e-2 (derived in the module docstring of the lse tests: the
 row sum is taken over weights rounded to bf16, relative error <= 2^-9, or over

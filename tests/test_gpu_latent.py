@@ -5,7 +5,7 @@ Bar for K_nope / V, derived from the arithmetic: bf16 x bf16 products are exact
 in fp32 and the 512-term fp32 sum adds at most ~5e-4 on these N(0, 1)-scaled
 values; the result is rounded to bf16 (half an ulp = 2^-9 relative).  So
 |gpu - oracle| <= 2^-8 |oracle| + 5e-4 element by element.  The attention that
-consumes them keeps the spec bar, 1e-2, against the oracle's attention
+consumes them keeps the bf16 accuracy bar, 1e-2, against the oracle's attention
 over the oracle's K_nope / V rounded to bf16 -- the type the attention takes
 them in (a value on a rounding boundary may round the other way on the GPU,
 a one-ulp input difference far inside the bar).

@@ -1,7 +1,7 @@
 """Null mask, log-sum-exp output and the merge of buffer rows on the GPU,
 against the float64 oracle.
 
-Bars (spec tolerances for the output, written here): max |gpu - oracle|
+Bars (the accuracy bars of the output, written here): max |gpu - oracle|
 <= 1e-2 with bf16 inputs and <= 6e-2 with float8_e4m3fn inputs.
 
 Log-sum-exp bars, derived from the arithmetic: scores are exact up to fp32

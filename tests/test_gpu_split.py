@@ -1,7 +1,7 @@
 """Split-query attention on the GPU (q_nope + q_rope, K_rope paged or
 contiguous) against the float64 oracle.
 
-Bars (spec tolerances): max |gpu - oracle| <= 1e-2 for bf16 inputs and
+Bars (the accuracy bars of the output): max |gpu - oracle| <= 1e-2 for bf16 inputs and
 <= 6e-2 for float8_e4m3fn q_nope / K / V.  The split bf16 query runs the same
 arithmetic as the one-tensor query, so those outputs must also match bit for bit.
 """
