@@ -28,20 +28,42 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile each source to an object in parallel, then link the shared library."""
+    import concurrent.futures
+    import tempfile
+
+    objdir = tempfile.mkdtemp(prefix="mla_build_")
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *compile_flags, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        return src, cmd, obj, res
+
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+        results = list(pool.map(compile_one, SOURCES))
+    objs = []
+    for src, cmd, obj, res in results:
+        out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({res.returncode}):\n{out}")
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stdout}{res.stderr}")
     os.replace(tmp, LIB)
+    for obj in objs:
+        os.remove(obj)
+    os.rmdir(objdir)
     return LIB
-
-
-if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
