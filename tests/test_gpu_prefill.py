@@ -44,7 +44,8 @@ SMALL = [
     dict(n=[130, 40, 0, 200], p=[10, 0, 5, 64], heads=16, ps=16, width=576, rope=512),  # heads in groups per XCD
     dict(n=[300], p=[20], heads=8, ps=64, width=576, rope=512),             # one sequence, one head per XCD
     dict(n=[70, 150, 3], p=[0, 0, 9], heads=24, ps=32, width=576, rope=512),  # 3 heads per XCD: partial group
-    dict(n=[90, 200, 17], p=[0, 64, 300], heads=40, ps=64, width=576, rope=512),  # 5 per XCD: groups of 4 and 1
+    dict(n=[90, 200, 17], p=[0, 64, 300], heads=40, ps=64, width=576, rope=512),  # 5 per XCD: one partial group
+    dict(n=[60, 130, 5], p=[0, 20, 100], heads=72, ps=16, width=576, rope=512),   # 9 per XCD: groups of 8 and 1
     dict(n=[130, 64], p=[40, 0], heads=128, ps=128, width=576, rope=512),   # DeepSeek-V3 head count, every output
 ]
 
