@@ -9,9 +9,12 @@
 // per workgroup of four waves, BN = 64 keys per tile, two direct-to-LDS stages,
 // S^T with one query per lane column) and an online softmax in the exp2 domain;
 // what differs:
-//   * the running max moves when a row's tile max exceeds it by more than
-//     RESCALE_LOG2, so every weight stays at most 2^RESCALE_LOG2 (below the
-//     e4m3 maximum of 448) on every tile;
+//   * every weight stays at most 2^RESCALE_LOG2 (below the e4m3 maximum of
+//     448): a tile that straddles the diagonal or the end of the keys moves the
+//     running reference when its max exceeds it by more than RESCALE_LOG2, and a
+//     fully visible tile keeps its weights against the reference as it stands
+//     when every lane's sum of them is at most 2^RESCALE_LOG2, else moves the
+//     reference up to the tile max and takes them again;
 //   * S^T = K . Q^T runs on the fp8 32x32x64 MFMA: two k-steps over the 128
 //     nope columns, then one over the 64 rope columns.  The nope partial sum is
 //     multiplied by s_knope / s_krope before the rope step, and
@@ -37,6 +40,7 @@ constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
 constexpr int DQK = 192, DNOPE = 128, DV = 128;
 constexpr float RESCALE_LOG2 = 8.0f;
+constexpr float WSUM_MAX = 256.0f;   // 2^RESCALE_LOG2: bound on a lane's e4m3 weight sum over a tile
 
 // LDS stage layout (bytes): rows of fp8, 16-byte chunks XOR-swizzled per row
 constexpr int KN_OFF = 0;                      // K_nope [64 rows][8 chunks]
@@ -312,6 +316,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
   const float ratio = QM == 0 ? s_kn / s_kr : s_q * s_kn / s_kr;
   const float thr = RESCALE_LOG2 / c;
   float m_run = -1e30f, mc = m_run * c, l_run = 0.f;
+  bool fresh = true;                                 // no tile computed yet
   f32x16 o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = f32x16{};
@@ -425,45 +430,35 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
         }
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_across_halves(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      m_run = m_new;
-      mc = m_run * c;
-      l_run *= alpha;
-      if constexpr (MFMA_ROWSUM) lsum[0] *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) o[d] *= alpha;
-    }
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float e[2][16];
+    auto weights = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-
-    if (full) {
-      // fp8 P: byte 16kb + r of this lane is key 32kb + 8(r/4) + 4hf + r%4
-      int pq[8];
+        for (int r = 0; r < 16; ++r) e[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+    };
+    // fp8 P: byte 16kb + r of this lane is key 32kb + 8(r/4) + 4hf + r%4; each
+    // word's four weights are packed as soon as they are taken, so the scores
+    // (kept for a second pass) and few weights are live at once
+    int pq[8];
+    float ps = 0.f;                                   // VALU row sum (this lane's 32 keys)
+    auto weights_fp8 = [&]() {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int kb = x >> 2, r = 4 * (x & 3);
+        float w4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w4[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + k], c, -mc));
         // the first conversion's untouched half is overwritten by the second, so
         // its "old" operand is any dead register (no copy of a zero needed)
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r], e[kb][r + 1], __builtin_bit_cast(int, e[kb][r]), false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[kb][r + 2], e[kb][r + 3], wd, true);
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(w4[0], w4[1], __builtin_bit_cast(int, w4[0]), false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(w4[2], w4[3], wd, true);
         pq[x] = wd;
       }
-      const i32x8 pop = {pq[0], pq[1], pq[2], pq[3], pq[4], pq[5], pq[6], pq[7]};
       if constexpr (MFMA_ROWSUM) {
-        lsum = mfma_fp8(ones8, pop, lsum);
+        lsum = mfma_fp8(ones8, i32x8{pq[0], pq[1], pq[2], pq[3], pq[4], pq[5], pq[6], pq[7]}, lsum);
       } else {
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -471,8 +466,56 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
           ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, false), ones, ps0, false);
           ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pq[x], 1.0f, true), ones, ps1, false);
         }
-        l_run += ps0 + ps1;
+        ps = ps0 + ps1;
       }
+    };
+    // A fully visible tile first takes its e4m3 weights against the running
+    // reference as it stands; when every lane's sum of them is at most
+    // 2^RESCALE_LOG2 (so no weight exceeds it: an overflowing conversion gives a
+    // NaN or 448, which fails the test too) they stand, and the tile needs no
+    // max.  Otherwise -- and on the wave's first tile, and on every tile that
+    // straddles the diagonal or the end of the keys -- the tile max is taken:
+    // a fully visible tile moves the reference up to it, a straddling one when
+    // it exceeds the reference by more than RESCALE_LOG2, and the weights are
+    // taken again.
+    bool redo = !full || fresh;
+    fresh = false;
+    float prev = 0.f;
+    if (!redo) {
+      if constexpr (MFMA_ROWSUM) prev = lsum[0];
+      weights_fp8();
+      const float d = MFMA_ROWSUM ? lsum[0] - prev : ps;
+      redo = __builtin_amdgcn_ballot_w64(!(d <= WSUM_MAX)) != 0;
+      if constexpr (MFMA_ROWSUM) {
+        if (redo) lsum[0] = prev;
+      }
+    }
+    if (redo) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max_across_halves(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > (full ? m_run : m_run + thr)) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        mc = m_run * c;
+        l_run *= alpha;
+        if constexpr (MFMA_ROWSUM) lsum[0] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] *= alpha;
+      }
+      if (full)
+        weights_fp8();
+      else
+        weights();
+    }
+
+    if (full) {
+      const i32x8 pop = {pq[0], pq[1], pq[2], pq[3], pq[4], pq[5], pq[6], pq[7]};
+      if constexpr (!MFMA_ROWSUM) l_run += ps;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         int va[8];

@@ -75,37 +75,50 @@ def _log2_scores(w, b, h):
     return w.softmax_scale * (q @ np.concatenate([kn, kr], axis=1).T) * np.log2(np.e)
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("scale", [2.0, -2.0])
-def test_fp8_running_max_moves_on_fully_visible_tiles(scale):
-    """A large softmax scale makes a row's running maximum jump by more than the
-    kernel's lazy-rescale threshold (8 in log2 units) on key tiles that every query
-    of the row's wave fully sees, after earlier such tiles have been summed -- the
-    tiles whose weights are e4m3 and whose row sums the matrix core accumulates.
-    The case first shows on the oracle's scores that such jumps occur, then
-    compares every output."""
+def test_fp8_running_reference_moves_on_fully_visible_tiles(scale, causal):
+    """The kernel takes a fully visible key tile's e4m3 weights against its running
+    reference and keeps them when every row's sum of them is at most 2^8 (so no
+    weight exceeds the e4m3 range); otherwise it takes the tile max, moves the
+    reference up to it and takes the weights again.  The reference is always the
+    score of a key seen earlier, so a tile whose weights against the exact running
+    maximum of the earlier keys sum to more than 2^8 takes that second pass
+    whatever the reference is.  A large softmax scale makes such tiles, some with
+    a single weight beyond 2^8 (a jump of the maximum by more than 8 in log2
+    units), after earlier tiles have been summed: under the causal mask on the
+    matrix core, under the null mask on the VALU.  The case first shows on the
+    oracle's scores that they occur, then compares every output."""
     spec = workloads.Spec("rescale8", 2, (0, 0), (0, 0), 2, 128, True, "fp8", row_width=576, rope_col=512,
                           seed=196)
     w = workloads.build(spec, n=[160, 40], p=[700, 90])
     w.softmax_scale = scale
     x = _log2_scores(w, 0, 0)
     p0 = int(w.p[0])
-    jumps = 0
+    ctx = x.shape[1]
+    second, jumps = 0, 0
     for i in range(x.shape[0]):
         wave_first = p0 + 32 * (i // 32)              # first query position of the row's wave
+        last = p0 + i if causal else ctx - 1          # the row's last visible key
         m = None
-        for kt in range((p0 + i) // 64 + 1):
-            keys = x[i, kt * 64:min((kt + 1) * 64, p0 + i + 1)]
+        for kt in range(last // 64 + 1):
+            keys = x[i, kt * 64:min((kt + 1) * 64, last + 1)]
             mx = keys.max()
-            full = kt * 64 + 63 <= wave_first
-            if m is not None and mx > m + 8.0 and full:
-                jumps += 1
+            full = (kt + 1) * 64 <= ctx and (not causal or kt * 64 + 63 <= wave_first)
+            if m is not None and full:
+                second += int(np.exp2(keys - m).sum() > 256.0)
+                jumps += int(mx > m + 8.0)
             m = mx if m is None else max(m, mx)
-    say(f"fp8 scale {scale}: {jumps} running-max jumps beyond the threshold on fully visible tiles")
-    assert jumps > 0
-    step = _run(w)
+    say(f"fp8 scale {scale} causal {causal}: {second} second passes on fully visible tiles, "
+        f"{jumps} of them with a weight beyond 2^8")
+    assert jumps > 0 and second > jumps
+    mask = "causal" if causal else "null"
+    step = PrefillStep(w, "cuda", mask=mask)
+    step.run()
+    torch.cuda.synchronize()
     bro, co, _ = check_plan(step, w)
-    ref = oracle_full(w, bro[0], co[0])
-    assert report(step.out.float().cpu().numpy(), ref, BAR_FP8, f"fp8rescale{scale}") <= BAR_FP8
+    ref = oracle_full(w, bro[0], co[0], mask=mask)
+    assert report(step.out.float().cpu().numpy(), ref, BAR_FP8, f"fp8rescale{scale}{mask}") <= BAR_FP8
 
 
 def test_fp8_workload_sampled():
