@@ -19,12 +19,12 @@
 //     nope columns, then one over the 64 rope columns.  The nope partial sum is
 //     multiplied by s_knope / s_krope before the rope step, and
 //     s_q * s_krope * |scale| * log2(e) is folded into the exp2 argument.
-//   * P.V on tiles every query of the wave fully sees runs on the same fp8
-//     MFMA: p (at most 2^RESCALE_LOG2) is rounded to e4m3 and the row sum is
-//     taken over the rounded values, so the weights stay exactly normalised.
-//     Tiles that straddle the causal diagonal or the end of the keys -- where a
-//     row has few keys and fp8 weights would be coarse -- use the bf16 MFMA with
-//     V converted exactly from e4m3 to bf16 and bf16 p.
+//   * P.V runs on the same fp8 MFMA: p (at most 2^RESCALE_LOG2) is rounded to
+//     e4m3 and the row sum is taken over the rounded values, so the weights stay
+//     exactly normalised.  A tile that straddles the causal diagonal or the end
+//     of the keys while some row of the wave sees fewer than PV8_MIN_KEYS keys
+//     -- where the few weights of such a row would be coarse -- uses the bf16
+//     MFMA instead, with V converted exactly from e4m3 to bf16 and bf16 p.
 //   * V is read transposed with ds_read_b64_tr_b8 (8 keys of one dv column per
 //     lane); s_v is applied to O in the epilogue.
 #include <type_traits>
@@ -40,6 +40,7 @@ constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
 constexpr int DQK = 192, DNOPE = 128, DV = 128;
 constexpr float RESCALE_LOG2 = 8.0f;
+constexpr int32_t PV8_MIN_KEYS = 128;
 constexpr float WSUM_MAX = 256.0f;   // 2^RESCALE_LOG2: bound on a lane's e4m3 weight sum over a tile
 
 // LDS stage layout (bytes): rows of fp8, 16-byte chunks XOR-swizzled per row
@@ -418,6 +419,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
       }
     }
     const bool full = (j0 + BN <= len) && (!causal || c0 + j0 + BN - 1 <= wq_first);
+    // e4m3 weights and P.V also on a straddling tile when every row of the wave
+    // sees at least PV8_MIN_KEYS keys in this call (its first row sees the
+    // fewest): its weights are then as coarse as those of any fully visible tile
+    const bool pv8 = full || min(causal ? p + iw0 - c0 + 1 : len, len) >= PV8_MIN_KEYS;
     if (!full) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -507,13 +512,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_fp8_kernel(PrefillArgs a) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) o[d] *= alpha;
       }
-      if (full)
+      if (pv8)
         weights_fp8();
       else
         weights();
     }
 
-    if (full) {
+    if (pv8) {
       const i32x8 pop = {pq[0], pq[1], pq[2], pq[3], pq[4], pq[5], pq[6], pq[7]};
       if constexpr (!MFMA_ROWSUM) l_run += ps;
 #pragma unroll
