@@ -18,8 +18,10 @@ configs  = each H=128 workload (dsv3, prefix, long, fp8): its attention launch
            timed alone (mean / median / min), TFLOP/s, fraction of its own
            dtype's MFMA peak, HBM traffic over algorithmic bytes, and its own
            bounded oracle sample.
-Also reported: plan / gather / attention times (mean, median, min over the timed
-steps), the attention time with L2 and MALL flushed by a 512 MiB write before
+Also reported: the attention time (mean, median, min over the timed steps, from
+the two events around each attention launch, the only events in the timed
+loop), plan / gather times (from events around them in a second run of the same
+steps after the timed one), the attention time with L2 and MALL flushed by a 512 MiB write before
 each launch (cold_cache), and the gather kernel's bandwidth on a >= 1 GiB
 paged cache of 576-wide bf16 rows (gather_bench).
 """
@@ -441,27 +443,38 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The timed steps carry two HIP events each, around the attention launch (its
+    # duration gives the roofline figure); every further event pair in the loop
+    # would add a few microseconds of its own to the measured step.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        e = ev[k]
+        step.plan()
+        step.gather(0)
+        ev[k][0].record(stream)
+        step.attention(0)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    attn_all = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    attn_ms = sum(attn_all) / args.steps
+    attn_best = attn_all[0]
+    attn_median = attn_all[len(attn_all) // 2]
+    # plan and gather times: the same launches, bracketed by events, after the timed steps
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        e = sev[k]
         e[0].record(stream)
         step.plan()
         e[1].record(stream)
         step.gather(0)
         e[2].record(stream)
         step.attention(0)
-        e[3].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    plan_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    gather_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    attn_all = sorted(e[2].elapsed_time(e[3]) for e in ev)
-    attn_ms = sum(attn_all) / args.steps
-    attn_best = attn_all[0]
-    attn_median = attn_all[len(attn_all) // 2]
+    plan_ms = sum(e[0].elapsed_time(e[1]) for e in sev) / args.steps
+    gather_ms = sum(e[1].elapsed_time(e[2]) for e in sev) / args.steps
 
     dtype = spec.dtype
     achieved = flops / (attn_ms * 1e-3) / 1e12
