@@ -50,6 +50,22 @@ def test_fp8_small_ragged_every_output(case):
     assert report(step.out.float().cpu().numpy(), ref, BAR_FP8, f"fp8small{case}") <= BAR_FP8
 
 
+@pytest.mark.parametrize("p", [95, 96, 127])
+def test_fp8_straddling_tiles_either_side_of_the_key_count_threshold(p):
+    """A straddling tile takes e4m3 weights and P.V when every row of its wave
+    sees at least 128 keys, else bf16 ones.  With a prefix of 95 keys the first
+    wave's first row sees 96 keys (bf16) and the second wave's first row exactly
+    128 (e4m3); with 96 the second wave's first row sees 129; with 127 the first
+    wave's first row sees exactly 128, so every wave takes e4m3.  Every output
+    against the oracle."""
+    spec = workloads.Spec("thr8", 1, (0, 0), (0, 0), 2, 32, True, "fp8", row_width=576, rope_col=512, seed=200 + p)
+    w = workloads.build(spec, n=[300], p=[p])
+    step = _run(w)
+    bro, co, _ = check_plan(step, w)
+    ref = oracle_full(w, bro[0], co[0])
+    assert report(step.out.float().cpu().numpy(), ref, BAR_FP8, f"fp8thr{p}") <= BAR_FP8
+
+
 @pytest.mark.parametrize("scale", [-0.0721687836, 0.0])
 def test_fp8_scale_sign_and_zero(scale):
     spec = workloads.Spec("scale8", 2, (0, 0), (0, 0), 3, 16, True, "fp8", row_width=576, rope_col=512, seed=190)
